@@ -1,0 +1,191 @@
+/*
+ * dsa.h — C ABI of the DSA sparse-attention layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one per MLA full-attention layer) runs, for every query row:
+ *   1. the lightning indexer: score every visible cached token with 32 light heads over
+ *      128-dim FP8 (or MXFP4) index keys                       -> dsa_indexer_scores
+ *   2. an exact top-k select (k <= 2048)                      -> dsa_topk
+ *   3. exact MLA attention of all 96 heads over only the selected latents
+ *                                                              -> sparse_mla_decode / _prefill
+ * Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" (§Sparse Attention in K3.1 Pro for the
+ * three steps and the 132-byte FP8 index key / 576-byte FP8 latent; §A KV cache for three kinds
+ * of state for the block-packed paged cache, its power-of-two block size, the NVFP4 latent and
+ * MXFP4 index-key variants, and block tables translated into kernel-page addresses; §Low-latency
+ * decode for the scorer + exact select that hands attention the physical KV rows;
+ * §AMD / Quantization: Native MXFP4 indexer for 68-byte MXFP4 keys scored on FP4 matrix
+ * instructions with FP32 accumulation).  The scoring rule is the DeepSeek-V3.2 lightning
+ * indexer's, to which the page defers:
+ *     score[r,s] = sum_h w[r,h] * ReLU(scale_s * q[r,h] . k[s]).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless the comment says "host".  The caller owns every
+ *     buffer (pool, tables, queries, outputs, workspaces); the library never allocates or frees
+ *     device memory and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and buffers must stay valid until it completes.
+ *   - Errors are returned, never thrown.  Host-side validation runs before anything is launched;
+ *     a failed call launches nothing.  dsa_last_error() gives a per-thread message.
+ *   - Out-of-range device data (a block id outside the pool, an index past a row's position) is
+ *     not checked on the device; results are then undefined.
+ *   - Identical inputs give bit-identical outputs.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef DSA_API
+#define DSA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned buffer, k out of range, ... */
+  DSA_ERR_UNSUPPORTED = 2, /* a format or shape this build does not implement */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+  DSA_ERR_HIP = 4          /* a HIP runtime call failed; dsa_last_error() has its text */
+} dsa_status;
+
+/* Index-key formats (page: FP8 keys of 132 B/token incl. scale; opt-in MXFP4 keys, 68 B). */
+enum { DSA_IKEY_FP8 = 0, DSA_IKEY_MXFP4 = 1 };
+/* Latent formats (page: FP8 latent, 576 B/token; NVFP4 latent). */
+enum { DSA_LATENT_FP8 = 0, DSA_LATENT_NVFP4 = 1 };
+
+/* Fixed model geometry (page: 32 indexer heads x 128 dims, top-2048, 96 attention heads; the
+ * MLA latent is 576 wide and its first 512 dims are the value). */
+enum {
+  DSA_INDEX_HEADS = 32,
+  DSA_INDEX_DIM = 128,
+  DSA_MLA_HEADS = 96,
+  DSA_MLA_DQK = 576,
+  DSA_MLA_DV = 512,
+  DSA_MAX_TOPK = 2048,
+  DSA_HIST_BINS = 2048,
+  DSA_MAX_ROWS_PER_SEQ = 8
+};
+
+/*
+ * Paged, block-packed KV pool (one layer).  The pool is num_blocks rows of row_bytes bytes; row
+ * b holds tokens [0, block_size) of whichever block the block tables map to b.  Inside a row
+ * the pages are structure-of-arrays, each starting 16-byte aligned at the given byte offset:
+ *   latent_format FP8:    latent       [bs][576] E4M3        at latent_off
+ *                         latent scale [bs] fp32             at latent_scale_off
+ *   latent_format NVFP4:  latent       [bs][288] packed E2M1 at latent_off  (element 2j is the
+ *                                                            low nibble of byte j)
+ *                         block scales [bs][36] E4M3 (one per 16 elements) at latent_scale_off
+ *                         value = E2M1 * block scale * latent_tensor_scale
+ *   ikey_format FP8:      keys         [bs][128] E4M3        at ikey_off
+ *                         key scale    [bs] fp32 (> 0)       at ikey_scale_off
+ *   ikey_format MXFP4:    keys         [bs][64] packed E2M1  at ikey_off
+ *                         block scales [bs][4] E8M0 (one per 32 elements) at ikey_scale_off
+ * row_bytes is a multiple of 256.  Token s of a sequence lives in row block_table[s / bs],
+ * slot s % bs; its physical row index is block_table[s / bs] * bs + s % bs.
+ */
+typedef struct dsa_kv_layout {
+  int32_t block_size;    /* tokens per block; this build supports 64 */
+  int32_t ikey_format;   /* DSA_IKEY_* */
+  int32_t latent_format; /* DSA_LATENT_* */
+  int32_t reserved;
+  int64_t row_bytes;
+  int64_t latent_off, latent_scale_off, ikey_off, ikey_scale_off;
+  int64_t num_blocks;        /* rows in the pool */
+  float latent_tensor_scale; /* NVFP4 only: the fp32 tensor scale (> 0); 1 otherwise */
+} dsa_kv_layout;
+
+/*
+ * Query rows of one call, grouped by sequence.  Row r sits at absolute position row_pos[r] and
+ * sees tokens [0, row_pos[r]] of its sequence (its own token included: the new token's key and
+ * latent are in the cache before the layer runs).  Several rows of one sequence (speculative
+ * verification, chunked prefill) read that sequence's keys once.
+ */
+typedef struct dsa_batch {
+  int32_t num_seqs;
+  int32_t num_rows;
+  int32_t max_rows_per_seq;   /* host: upper bound on rows of any one sequence */
+  int32_t max_blocks_per_seq; /* host: leading dimension of block_table */
+  int64_t max_context;        /* host: upper bound on row_pos[r] + 1 over all rows */
+  const int32_t* block_table;   /* [num_seqs * max_blocks_per_seq] pool row ids */
+  const int32_t* seq_row_start; /* [num_seqs + 1] rows of sequence b: [start[b], start[b+1]) */
+  const int32_t* row_pos;       /* [num_rows] */
+} dsa_batch;
+
+/* Fill *out (host) with the pool layout for the given formats (block_size must be 64).
+ * Returns INVALID_ARG for a null pointer or bad value, UNSUPPORTED for another block size. */
+DSA_API dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, int32_t latent_format,
+                              int32_t block_size, int64_t num_blocks, float latent_tensor_scale);
+
+/*
+ * Step 1 — lightning-indexer scores of every visible token, for every row.
+ *   q_idx  [num_rows][32][128] E4M3 indexer queries (any quantisation scale folded into w)
+ *   w      [num_rows][32] fp32 head weights
+ *   scores [num_rows][ld_scores] fp32 output; entries [0, row_pos[r]] are written, the rest are
+ *          left untouched.  ld_scores >= max_context.
+ *   hist   [num_rows][DSA_HIST_BINS] uint32 output or NULL: histogram of the top 11 bits of each
+ *          written score's order-preserving key, consumed by dsa_topk to skip one pass over the
+ *          scores.  Only available on the decode path (max_rows_per_seq <= 8); must be NULL
+ *          otherwise.
+ * Decode and speculative decode (max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ) stream the index keys
+ * once per sequence and score all of that sequence's rows from each key read.  Prefill chunks
+ * (more rows per sequence; FP8 keys only) run as a dense FP8 matrix contraction of row tiles
+ * against key tiles.
+ * Exactness: key products are exact and accumulate in fp32; scale_s > 0 is applied after the
+ * head sum (equal to applying it inside each ReLU whenever the sums are exact).
+ */
+DSA_API dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                              const uint8_t* q_idx, const float* w, float* scores,
+                              int64_t ld_scores, uint32_t* hist, void* stream);
+
+/*
+ * Step 2 — exact top-k per row (page: keep the 2,048 highest-scoring tokens).  Order: score
+ * descending, token index ascending (a tie goes to the lower index); -0 equals +0.  NaN scores
+ * are not supported.
+ *   scores/ld_scores/hist as produced by step 1 (hist may be NULL: one more pass is then made)
+ *   k in [1, DSA_MAX_TOPK]
+ *   idx   [num_rows][k] int32 output: the selected token indices in ascending order, then -1
+ *   count [num_rows] int32 output: min(k, row_pos[r] + 1)
+ *   phys  [num_rows][k] int32 output or NULL: physical pool rows (block * bs + slot) of idx,
+ *         -1 padded (kv is required when phys is not NULL)
+ */
+DSA_API dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float* scores,
+                    int64_t ld_scores, const uint32_t* hist, int32_t k, int32_t* idx,
+                    int32_t* count, int32_t* phys, void* stream);
+
+/* Workspace bytes sparse_mla_decode needs for num_rows rows and top-k k. */
+DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k);
+
+/*
+ * Step 3 — exact MLA attention over the selected latents (page: every query head attends
+ * exactly over only the selected tokens; the latent is shared by all heads).  For row r and
+ * head h, over j in idx[r][0..k) with idx >= 0:
+ *   c_j = dequantised latent of token idx[r][j] (FP8 code * token scale, or NVFP4)
+ *   logit_j = softmax_scale * q[r,h] . c_j ;  p = softmax(logit)
+ *   out[r,h] = sum_j p_j c_j[0:512] ;  lse[r,h] = max + ln sum exp(logit - max)
+ *   q    [num_rows][96][576] bf16;  idx [num_rows][k] from dsa_topk
+ *   out  [num_rows][96][512] bf16 output;  lse [num_rows][96] fp32 output or NULL
+ *   workspace: device scratch of at least sparse_mla_workspace_bytes(num_rows, k) bytes
+ * A row with no selected token gets out = 0 and lse = -inf.
+ * The decode variant splits each row's selected set over several workgroups and merges the
+ * partial results by log-sum-exp; the prefill variant (for thousands of rows) gives each row one
+ * workgroup across all heads and needs no workspace (it may be NULL).
+ */
+DSA_API dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                             const uint16_t* q, const int32_t* idx, int32_t k,
+                             float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+DSA_API dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                              const uint16_t* q, const int32_t* idx, int32_t k,
+                              float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Text of a status code, and the calling thread's last error message ("" if none). */
+DSA_API const char* dsa_status_string(dsa_status s);
+DSA_API const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

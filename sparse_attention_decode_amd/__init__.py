@@ -1,0 +1,16 @@
+"""DSA sparse-attention layer (lightning indexer -> exact top-k -> sparse MLA) for MI355X.
+
+The compute lives in libdsa.so (HIP kernels for gfx950 behind the C ABI of include/dsa.h); this
+package is its Python binding plus a small driver that runs the three steps on one stream.
+Source of the method: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Sparse Attention in K3.1
+Pro.
+"""
+from ._lib import (DSAError, DeviceBatch, KVLayout, kv_layout, dsa_indexer_scores, dsa_topk,
+                   sparse_mla_decode, sparse_mla_prefill, sparse_mla_workspace_bytes, lib,
+                   IKEY_FP8, IKEY_MXFP4, LATENT_FP8, LATENT_NVFP4, MAX_TOPK, HIST_BINS,
+                   MAX_ROWS_PER_SEQ, INDEX_HEADS, INDEX_DIM, MLA_HEADS, MLA_DQK, MLA_DV, EXPORTS)
+from .layer import DSALayer
+
+__all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scores", "dsa_topk",
+           "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_workspace_bytes", "lib",
+           "DSALayer", "EXPORTS"]

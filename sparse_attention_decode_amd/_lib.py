@@ -1,0 +1,161 @@
+"""ctypes binding of libdsa.so (include/dsa.h).  Argument marshalling only: every step of the
+layer runs in the HIP kernels behind the C ABI.  Tensors are torch tensors on the GPU; streams
+are torch CUDA(HIP) streams (the current stream by default)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+IKEY_FP8, IKEY_MXFP4 = 0, 1
+LATENT_FP8, LATENT_NVFP4 = 0, 1
+INDEX_HEADS, INDEX_DIM, MLA_HEADS, MLA_DQK, MLA_DV = 32, 128, 96, 576, 512
+MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
+
+# Every symbol include/dsa.h declares.
+EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk", "sparse_mla_workspace_bytes",
+           "sparse_mla_decode", "sparse_mla_prefill", "dsa_status_string", "dsa_last_error")
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+class KVLayout(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("ikey_format", ctypes.c_int32),
+                ("latent_format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int64), ("latent_off", ctypes.c_int64),
+                ("latent_scale_off", ctypes.c_int64), ("ikey_off", ctypes.c_int64),
+                ("ikey_scale_off", ctypes.c_int64), ("num_blocks", ctypes.c_int64),
+                ("latent_tensor_scale", ctypes.c_float)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("max_rows_per_seq", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_context", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("seq_row_start", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdsa.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.dsa_kv_layout_init.restype = i32
+        L.dsa_kv_layout_init.argtypes = [ctypes.POINTER(KVLayout), i32, i32, i32, i64, f32]
+        L.dsa_indexer_scores.restype = i32
+        L.dsa_indexer_scores.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp,
+                                         vp, vp, i64, vp, vp]
+        L.dsa_topk.restype = i32
+        L.dsa_topk.argtypes = [ctypes.POINTER(KVLayout), ctypes.POINTER(Batch), vp, i64, vp, i32,
+                               vp, vp, vp, vp]
+        L.sparse_mla_workspace_bytes.restype = ctypes.c_size_t
+        L.sparse_mla_workspace_bytes.argtypes = [i32, i32]
+        for fn in ("sparse_mla_decode", "sparse_mla_prefill"):
+            f = getattr(L, fn)
+            f.restype = i32
+            f.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp, vp, i32, f32,
+                          vp, vp, vp, ctypes.c_size_t, vp]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int, fn: str):
+    if status != DSA_OK:
+        raise DSAError(status, fn, lib().dsa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kv_layout(ikey_format: int, latent_format: int, num_blocks: int,
+              latent_tensor_scale: float = 1.0, block_size: int = 64) -> KVLayout:
+    kv = KVLayout()
+    _check(lib().dsa_kv_layout_init(ctypes.byref(kv), ikey_format, latent_format, block_size,
+                                    num_blocks, latent_tensor_scale), "dsa_kv_layout_init")
+    return kv
+
+
+class DeviceBatch:
+    """A dsa_batch plus the device tensors it points at (kept alive here)."""
+
+    def __init__(self, block_table, seq_row_start, row_pos, max_rows_per_seq: int,
+                 max_context: int):
+        self.block_table, self.seq_row_start, self.row_pos = block_table, seq_row_start, row_pos
+        b = Batch()
+        b.num_seqs = seq_row_start.numel() - 1
+        b.num_rows = row_pos.numel()
+        b.max_rows_per_seq = int(max_rows_per_seq)
+        b.max_blocks_per_seq = block_table.shape[1]
+        b.max_context = int(max_context)
+        b.block_table = block_table.data_ptr()
+        b.seq_row_start = seq_row_start.data_ptr()
+        b.row_pos = row_pos.data_ptr()
+        self.c = b
+
+    @property
+    def num_rows(self) -> int:
+        return self.c.num_rows
+
+
+def dsa_indexer_scores(kv: KVLayout, pool, batch: DeviceBatch, q_idx, w, scores, hist=None,
+                       stream=None):
+    _check(lib().dsa_indexer_scores(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c),
+                                    _ptr(q_idx), _ptr(w), _ptr(scores), scores.stride(0),
+                                    _ptr(hist), _stream(stream)), "dsa_indexer_scores")
+
+
+def dsa_topk(kv: KVLayout | None, batch: DeviceBatch, scores, hist, k: int, idx, count,
+             phys=None, stream=None):
+    _check(lib().dsa_topk(ctypes.byref(kv) if kv is not None else None, ctypes.byref(batch.c),
+                          _ptr(scores), scores.stride(0), _ptr(hist), k, _ptr(idx), _ptr(count),
+                          _ptr(phys), _stream(stream)), "dsa_topk")
+
+
+def sparse_mla_workspace_bytes(num_rows: int, k: int) -> int:
+    return int(lib().sparse_mla_workspace_bytes(num_rows, k))
+
+
+def _mla(fn: str, kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace, stream):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib(), fn)(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c), _ptr(q),
+                              _ptr(idx), k, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                              ws_bytes, _stream(stream)), fn)
+
+
+def sparse_mla_decode(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None, workspace=None,
+                      stream=None):
+    _mla("sparse_mla_decode", kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+         stream)
+
+
+def sparse_mla_prefill(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None, workspace=None,
+                       stream=None):
+    _mla("sparse_mla_prefill", kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+         stream)

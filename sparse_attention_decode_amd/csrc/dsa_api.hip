@@ -1,0 +1,266 @@
+// C ABI of the DSA layer: argument validation, pool layout, and kernel dispatch on the caller's
+// stream.  Declarations and argument contracts are in include/dsa.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+dsa_status check_layout(const dsa_kv_layout* kv, const void* pool) {
+  if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is NULL");
+  if (!pool) return fail(DSA_ERR_INVALID_ARG, "pool is NULL");
+  if (!aligned(pool, 256)) return fail(DSA_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+  if (kv->block_size != 64)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d (only 64 is built)", kv->block_size);
+  if (kv->ikey_format != DSA_IKEY_FP8 && kv->ikey_format != DSA_IKEY_MXFP4)
+    return fail(DSA_ERR_INVALID_ARG, "unknown ikey_format %d", kv->ikey_format);
+  if (kv->latent_format != DSA_LATENT_FP8 && kv->latent_format != DSA_LATENT_NVFP4)
+    return fail(DSA_ERR_INVALID_ARG, "unknown latent_format %d", kv->latent_format);
+  const int64_t offs[4] = {kv->latent_off, kv->latent_scale_off, kv->ikey_off, kv->ikey_scale_off};
+  for (int i = 0; i < 4; ++i)
+    if (offs[i] < 0 || offs[i] % 16 || offs[i] >= kv->row_bytes)
+      return fail(DSA_ERR_INVALID_ARG, "page offset %lld not 16-aligned inside the row",
+                  (long long)offs[i]);
+  if (kv->row_bytes <= 0 || kv->row_bytes % 256)
+    return fail(DSA_ERR_INVALID_ARG, "row_bytes %lld must be a positive multiple of 256",
+                (long long)kv->row_bytes);
+  if (kv->num_blocks <= 0) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (kv->latent_format == DSA_LATENT_NVFP4 &&
+      !(kv->latent_tensor_scale > 0.f && isfinite(kv->latent_tensor_scale)))
+    return fail(DSA_ERR_INVALID_ARG, "NVFP4 tensor scale must be finite and positive");
+  return DSA_OK;
+}
+
+dsa_status check_batch(const dsa_batch* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+  if (b->num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "num_rows must be >= 0");
+  if (b->max_rows_per_seq < 1) return fail(DSA_ERR_INVALID_ARG, "max_rows_per_seq must be >= 1");
+  if (b->max_context < 1) return fail(DSA_ERR_INVALID_ARG, "max_context must be >= 1");
+  if (b->max_context > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "max_context too large");
+  if ((int64_t)b->max_blocks_per_seq * 64 < b->max_context)
+    return fail(DSA_ERR_INVALID_ARG, "max_blocks_per_seq * 64 < max_context");
+  if (!b->block_table || !b->seq_row_start || !b->row_pos)
+    return fail(DSA_ERR_INVALID_ARG, "block_table, seq_row_start and row_pos must be non-NULL");
+  return DSA_OK;
+}
+
+dsa::PoolView pool_view(const dsa_kv_layout* kv, const void* pool) {
+  dsa::PoolView p;
+  p.base = static_cast<const uint8_t*>(pool);
+  p.row_bytes = kv->row_bytes;
+  p.lat_off = kv->latent_off;
+  p.lat_scale_off = kv->latent_scale_off;
+  p.ikey_off = kv->ikey_off;
+  p.ikey_scale_off = kv->ikey_scale_off;
+  return p;
+}
+
+dsa::BatchView batch_view(const dsa_batch* b) {
+  dsa::BatchView v;
+  v.block_table = b->block_table;
+  v.ld_bt = b->max_blocks_per_seq;
+  v.seq_row_start = b->seq_row_start;
+  v.row_pos = b->row_pos;
+  v.num_seqs = b->num_seqs;
+  v.num_rows = b->num_rows;
+  return v;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                      const uint16_t* q, const int32_t* idx, int32_t k, float softmax_scale,
+                      uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, bool prefill) {
+  dsa_status st = check_layout(kv, pool);
+  if (st != DSA_OK) return st;
+  if ((st = check_batch(batch)) != DSA_OK) return st;
+  if (!q || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
+  if (!isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale not finite");
+  if (batch->num_rows == 0) return DSA_OK;
+  dsa::MlaArgs a;
+  a.pool = pool_view(kv, pool);
+  a.batch = batch_view(batch);
+  a.q = q;
+  a.idx = idx;
+  a.k = k;
+  a.softmax_scale = softmax_scale;
+  a.tensor_scale = kv->latent_format == DSA_LATENT_NVFP4 ? kv->latent_tensor_scale : 1.f;
+  a.out = out;
+  a.lse = lse;
+  a.nsplit = prefill ? 1 : dsa::mla_num_splits(batch->num_rows, k);
+  a.tokens_per_split = (int32_t)align_up((k + a.nsplit - 1) / a.nsplit, 32);
+  a.nsplit = (k + a.tokens_per_split - 1) / a.tokens_per_split;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (a.nsplit > 1) {
+    const size_t need = dsa::mla_workspace_bytes(batch->num_rows, k);
+    if (!workspace || workspace_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)batch->num_rows * a.nsplit * DSA_MLA_HEADS * DSA_MLA_DV;
+  }
+  return hip_status(dsa::launch_sparse_mla(a, kv->latent_format, stream),
+                    prefill ? "sparse_mla_prefill launch" : "sparse_mla_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, int32_t latent_format,
+                              int32_t block_size, int64_t num_blocks, float latent_tensor_scale) {
+  g_err[0] = 0;
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is NULL");
+  if (block_size != 64) return fail(DSA_ERR_UNSUPPORTED, "block_size %d (only 64 is built)", block_size);
+  if (ikey_format != DSA_IKEY_FP8 && ikey_format != DSA_IKEY_MXFP4)
+    return fail(DSA_ERR_INVALID_ARG, "unknown ikey_format %d", ikey_format);
+  if (latent_format != DSA_LATENT_FP8 && latent_format != DSA_LATENT_NVFP4)
+    return fail(DSA_ERR_INVALID_ARG, "unknown latent_format %d", latent_format);
+  if (num_blocks <= 0) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (latent_format == DSA_LATENT_NVFP4 && !(latent_tensor_scale > 0.f && isfinite(latent_tensor_scale)))
+    return fail(DSA_ERR_INVALID_ARG, "NVFP4 tensor scale must be finite and positive");
+  memset(out, 0, sizeof(*out));
+  const int64_t bs = block_size;
+  int64_t off = 0;
+  out->block_size = block_size;
+  out->ikey_format = ikey_format;
+  out->latent_format = latent_format;
+  out->latent_off = off;
+  off += bs * (latent_format == DSA_LATENT_FP8 ? DSA_MLA_DQK : DSA_MLA_DQK / 2);
+  out->latent_scale_off = off = align_up(off, 16);
+  off += bs * (latent_format == DSA_LATENT_FP8 ? 4 : DSA_MLA_DQK / 16);
+  out->ikey_off = off = align_up(off, 16);
+  off += bs * (ikey_format == DSA_IKEY_FP8 ? DSA_INDEX_DIM : DSA_INDEX_DIM / 2);
+  out->ikey_scale_off = off = align_up(off, 16);
+  off += bs * (ikey_format == DSA_IKEY_FP8 ? 4 : DSA_INDEX_DIM / 32);
+  out->row_bytes = align_up(off, 256);
+  out->num_blocks = num_blocks;
+  out->latent_tensor_scale = latent_format == DSA_LATENT_NVFP4 ? latent_tensor_scale : 1.f;
+  return DSA_OK;
+}
+
+dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                              const uint8_t* q_idx, const float* w, float* scores,
+                              int64_t ld_scores, uint32_t* hist, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_layout(kv, pool);
+  if (st != DSA_OK) return st;
+  if ((st = check_batch(batch)) != DSA_OK) return st;
+  if (!q_idx || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "q_idx, w and scores must be non-NULL");
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(scores, 4))
+    return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte aligned");
+  if (ld_scores < batch->max_context)
+    return fail(DSA_ERR_INVALID_ARG, "ld_scores %lld < max_context %lld", (long long)ld_scores,
+                (long long)batch->max_context);
+  if (batch->num_rows == 0) return DSA_OK;
+  dsa::IndexerArgs a;
+  a.pool = pool_view(kv, pool);
+  a.batch = batch_view(batch);
+  a.q = q_idx;
+  a.w = w;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.hist = hist;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ)
+    return hip_status(dsa::launch_indexer_decode(a, kv->ikey_format, batch->max_rows_per_seq,
+                                                 batch->max_context, s),
+                      "indexer launch");
+  if (hist) return fail(DSA_ERR_INVALID_ARG, "hist must be NULL on the prefill path");
+  if (kv->ikey_format != DSA_IKEY_FP8)
+    return fail(DSA_ERR_UNSUPPORTED, "prefill indexer is built for FP8 keys only");
+  return hip_status(dsa::launch_indexer_prefill(a, batch->max_context, batch->max_rows_per_seq, s),
+                    "prefill indexer launch");
+}
+
+dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float* scores,
+                    int64_t ld_scores, const uint32_t* hist, int32_t k, int32_t* idx,
+                    int32_t* count, int32_t* phys, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (!scores || !idx || !count) return fail(DSA_ERR_INVALID_ARG, "scores, idx and count must be non-NULL");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
+  if (ld_scores < batch->max_context)
+    return fail(DSA_ERR_INVALID_ARG, "ld_scores %lld < max_context", (long long)ld_scores);
+  if (phys) {
+    if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is required for phys rows");
+    if (kv->block_size != 64) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
+  }
+  if (batch->num_rows == 0) return DSA_OK;
+  dsa::TopkArgs a;
+  a.batch = batch_view(batch);
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.hist = hist;
+  a.k = k;
+  a.idx = idx;
+  a.count = count;
+  a.phys = phys;
+  return hip_status(dsa::launch_topk(a, static_cast<hipStream_t>(stream)), "topk launch");
+}
+
+size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k) {
+  if (num_rows <= 0 || k < 1) return 0;
+  return dsa::mla_workspace_bytes(num_rows, k > DSA_MAX_TOPK ? DSA_MAX_TOPK : k);
+}
+
+dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                             const uint16_t* q, const int32_t* idx, int32_t k,
+                             float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return mla_common(kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                              const uint16_t* q, const int32_t* idx, int32_t k,
+                              float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return mla_common(kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), true);
+}
+
+}  // extern "C"

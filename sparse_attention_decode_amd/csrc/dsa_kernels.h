@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI layer (dsa_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa_device.h"
+
+namespace dsa {
+
+struct BatchView {
+  const int32_t* block_table;
+  int64_t ld_bt;
+  const int32_t* seq_row_start;
+  const int32_t* row_pos;
+  int32_t num_seqs, num_rows;
+};
+
+struct IndexerArgs {
+  PoolView pool;
+  BatchView batch;
+  const uint8_t* q;  // [R][32][128] e4m3
+  const float* w;    // [R][32]
+  float* scores;     // [R][ld]
+  int64_t ld;
+  uint32_t* hist;    // [R][2048] or null
+  int32_t tiles_per_seq;  // row tiles per sequence (1 on the decode path)
+};
+
+// Decode / speculative decode scorer: grid (chunks, num_seqs).
+hipError_t launch_indexer_decode(const IndexerArgs& a, int ikey_fmt, int rows_per_seq,
+                                 int64_t max_context, hipStream_t s);
+// Prefill scorer (dense FP8 contraction of row tiles x key tiles).
+hipError_t launch_indexer_prefill(const IndexerArgs& a, int64_t max_context,
+                                  int32_t max_rows_per_seq, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+
+struct TopkArgs {
+  BatchView batch;
+  const float* scores;
+  int64_t ld;
+  const uint32_t* hist;  // or null
+  int32_t k;
+  int32_t* idx;
+  int32_t* count;
+  int32_t* phys;  // or null
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct MlaArgs {
+  PoolView pool;
+  BatchView batch;
+  const uint16_t* q;  // [R][96][576] bf16
+  const int32_t* idx; // [R][k]
+  int32_t k;
+  float softmax_scale;
+  float tensor_scale;  // NVFP4 latent tensor scale (1 for FP8)
+  uint16_t* out;       // [R][96][512] bf16
+  float* lse;          // [R][96] or null
+  float* part_o;       // [R][nsplit][96][512] fp32 (split path)
+  float* part_ml;      // [R][nsplit][96][2] fp32 (split path)
+  int32_t nsplit;
+  int32_t tokens_per_split;
+};
+int mla_num_splits(int32_t num_rows, int32_t k);
+size_t mla_workspace_bytes(int32_t num_rows, int32_t k);
+hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s);
+
+}  // namespace dsa

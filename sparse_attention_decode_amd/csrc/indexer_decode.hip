@@ -1,0 +1,219 @@
+// Lightning-indexer scorer for decode and speculative decode.
+//
+// Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Sparse Attention in K3.1 Pro (every
+// earlier token is scored for each query by 32 light heads over one FP8 key of 132 bytes with its
+// scale; long-context decode is bound by memory bandwidth); §AMD / Quantization: Native MXFP4
+// indexer (68-byte MXFP4 keys scored on FP4 matrix instructions with FP32 accumulation and a
+// weighted reduction across heads; keys reused across the query rows of a speculative
+// verification step).  Scoring rule (DeepSeek-V3.2 lightning indexer, which the page defers to):
+//     score[r,s] = sum_h w[r,h] * ReLU(scale_s * q[r,h] . k[s])
+// computed here as scale_s * sum_h w[r,h] * ReLU(q[r,h] . k[s]) (scale_s > 0).
+//
+// Design (gfx950): the key pages are the only large stream.  A workgroup owns a contiguous chunk
+// of one sequence's blocks; each wave pulls whole 64-token key pages straight from HBM into MFMA
+// operand registers (no LDS staging: each key byte is used by exactly one lane) and scores every
+// row of its sequence from that single read.  The query rows are the MFMA A operand (M = 32 heads
+// per row), keys the B operand (N = 16 tokens per tile, K = 128 dims in one instruction), so the
+// head reduction (ReLU, x w, sum over 32 heads) is 8 lane-local terms plus two cross-lane adds.
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kThreads = 256;         // 4 waves
+constexpr int kBlocksPerWave = 4;     // 64-token pages per wave per workgroup
+constexpr int kBlocksPerWG = kBlocksPerWave * (kThreads / kWave);
+constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
+
+// Operand fragments of one 16-token tile.
+struct KeyFrag {
+  v8i b;       // MFMA B operand
+  int escale;  // MXFP4: E8M0 scale of (token, K block l/16)
+  float scale; // FP8: scale_s of the lane's token
+};
+
+template <int KFMT>
+__device__ __forceinline__ KeyFrag load_key_frag(const uint8_t* row, const PoolView& p, int n,
+                                                 int g) {
+  KeyFrag f;
+  if (KFMT == DSA_IKEY_FP8) {
+    const uint8_t* k = row + p.ikey_off + n * DSA_INDEX_DIM;
+    uint4 lo = *reinterpret_cast<const uint4*>(k + 16 * g);
+    uint4 hi = *reinterpret_cast<const uint4*>(k + 64 + 16 * g);
+    f.b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+              (int)hi.w};
+    f.scale = *reinterpret_cast<const float*>(row + p.ikey_scale_off + n * 4);
+    f.escale = 127;
+  } else {
+    const uint8_t* k = row + p.ikey_off + n * (DSA_INDEX_DIM / 2);
+    uint4 v = *reinterpret_cast<const uint4*>(k + 16 * g);
+    f.b = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    f.escale = row[p.ikey_scale_off + n * 4 + g];
+    f.scale = 1.0f;
+  }
+  return f;
+}
+
+template <int R, int KFMT, bool HIST>
+__global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a) {
+  __shared__ uint32_t s_hist[HIST ? R * kBins : 1];
+  // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
+  const int seq = blockIdx.y / a.tiles_per_seq;
+  const int tile = blockIdx.y % a.tiles_per_seq;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+
+  const int r0 = a.batch.seq_row_start[seq] + tile * R;
+  const int nr = min(R, a.batch.seq_row_start[seq + 1] - r0);
+  if (nr <= 0) return;
+  int pos[R];
+  int L = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pos[r] = r < nr ? a.batch.row_pos[r0 + r] : -1;
+    L = max(L, pos[r] + 1);
+  }
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int blk0 = blockIdx.x * kBlocksPerWG;
+  if (blk0 >= nblk) return;  // whole workgroup past this sequence's end
+
+  constexpr bool use_hist = HIST;
+  if (use_hist) {
+    for (int i = tid; i < R * kBins; i += kThreads) s_hist[i] = 0;
+    __syncthreads();
+  }
+
+  // Query fragments (A operand, FP8 layout) and the head weights of the lane's result rows.
+  v8i qa[R][2];
+  float wv[R][2][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = r0 + min(r, max(nr - 1, 0));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint8_t* qr = a.q + ((int64_t)row * DSA_INDEX_HEADS + 16 * mt + c) * DSA_INDEX_DIM;
+      uint4 lo = *reinterpret_cast<const uint4*>(qr + 16 * g);
+      uint4 hi = *reinterpret_cast<const uint4*>(qr + 64 + 16 * g);
+      qa[r][mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y,
+                      (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wv[r][mt][i] = a.w[(int64_t)row * DSA_INDEX_HEADS + 16 * mt + 4 * g + i];
+    }
+  }
+
+  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
+  for (int ib = 0; ib < kBlocksPerWave; ++ib) {
+    const int blk = blk0 + ib * (kThreads / kWave) + wave;
+    if (blk >= nblk) break;
+    const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
+    KeyFrag f[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int s = blk * kBlock + 16 * nt + c;  // token of this lane's column
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r >= nr) break;
+        v4f z = {0.f, 0.f, 0.f, 0.f};
+        v4f acc0, acc1;
+        if (KFMT == DSA_IKEY_FP8) {
+          acc0 = mfma_fp8(qa[r][0], f[nt].b, z);
+          acc1 = mfma_fp8(qa[r][1], f[nt].b, z);
+        } else {
+          acc0 = mfma_fp8_fp4(qa[r][0], f[nt].b, z, 127, f[nt].escale);
+          acc1 = mfma_fp8_fp4(qa[r][1], f[nt].b, z, 127, f[nt].escale);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          part += wv[r][0][i] * fmaxf(acc0[i], 0.f);
+          part += wv[r][1][i] * fmaxf(acc1[i], 0.f);
+        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        const float score = part * f[nt].scale;
+        if (g == (r & 3) && s <= pos[r]) {
+          a.scores[(int64_t)(r0 + r) * a.ld + s] = score;
+          if (use_hist) atomicAdd(&s_hist[r * kBins + (order_key(score) >> 21)], 1u);
+        }
+      }
+    }
+  }
+
+  if (use_hist) {
+    __syncthreads();
+    for (int i = tid; i < nr * kBins; i += kThreads) {
+      const uint32_t v = s_hist[i];
+      if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
+    }
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+template <int KFMT>
+hipError_t launch_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s) {
+  switch (rows) {
+#define DSA_CASE(R)                                                                          \
+  case R:                                                                                    \
+    if (a.hist)                                                                              \
+      hipLaunchKernelGGL((indexer_decode_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((indexer_decode_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
+    break;
+    DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7)
+    DSA_CASE(8)
+#undef DSA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_per_seq,
+                                 int64_t max_context, hipStream_t s) {
+  IndexerArgs a = a0;
+  a.tiles_per_seq = 1;
+  if (a.hist) {
+    hipError_t e = launch_zero_u32(a.hist, (int64_t)a.batch.num_rows * kBins, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nblk = (max_context + kBlock - 1) / kBlock;
+  dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)a.batch.num_seqs);
+  return ikey_fmt == DSA_IKEY_FP8 ? launch_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
+                                  : launch_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
+}
+
+// Prefill: the rows of a sequence are cut into tiles of 8 (M = 256 head-rows per MFMA tile
+// column); each workgroup contracts one row tile with one chunk of key pages.  Key pages are
+// re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
+hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
+                                  int32_t max_rows_per_seq, hipStream_t s) {
+  IndexerArgs a = a0;
+  constexpr int R = DSA_MAX_ROWS_PER_SEQ;
+  a.tiles_per_seq = (max_rows_per_seq + R - 1) / R;
+  a.hist = nullptr;
+  const int64_t nblk = (max_context + kBlock - 1) / kBlock;
+  const int64_t gy = (int64_t)a.batch.num_seqs * a.tiles_per_seq;
+  if (gy > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)gy);
+  return launch_rows<DSA_IKEY_FP8>(a, R, grid, s);
+}
+
+}  // namespace dsa

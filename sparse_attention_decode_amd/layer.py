@@ -1,0 +1,53 @@
+"""One DSA layer step on one stream: scores -> top-k -> sparse MLA, with its device buffers."""
+from __future__ import annotations
+
+import math
+
+from . import _lib as L
+
+
+class DSALayer:
+    """Owns the per-call device buffers for a fixed batch shape and runs the three C-ABI steps.
+
+    kv: KVLayout of the pool; batch: DeviceBatch; k: top-k; prefill: use the prefill variant of
+    sparse MLA (one workgroup per row, no split).  Buffers are allocated once here (torch), never
+    inside run()."""
+
+    def __init__(self, kv: L.KVLayout, batch: L.DeviceBatch, k: int = 2048,
+                 softmax_scale: float = 1.0 / math.sqrt(192.0), prefill: bool = False,
+                 use_hist: bool | None = None, device="cuda"):
+        import torch
+        self.kv, self.batch, self.k, self.softmax_scale = kv, batch, k, softmax_scale
+        self.prefill = prefill
+        R = batch.num_rows
+        self.ld = (batch.c.max_context + 63) // 64 * 64
+        decode_path = batch.c.max_rows_per_seq <= L.MAX_ROWS_PER_SEQ
+        self.use_hist = decode_path if use_hist is None else (use_hist and decode_path)
+        self.scores = torch.empty((R, self.ld), dtype=torch.float32, device=device)
+        self.hist = (torch.empty((R, L.HIST_BINS), dtype=torch.int32, device=device)
+                     if self.use_hist else None)
+        self.idx = torch.empty((R, k), dtype=torch.int32, device=device)
+        self.count = torch.empty((R,), dtype=torch.int32, device=device)
+        self.out = torch.empty((R, L.MLA_HEADS, L.MLA_DV), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((R, L.MLA_HEADS), dtype=torch.float32, device=device)
+        nbytes = 0 if prefill else L.sparse_mla_workspace_bytes(R, k)
+        self.workspace = (torch.empty((max(nbytes, 16) + 15) // 16 * 4, dtype=torch.float32,
+                                      device=device) if nbytes else None)
+
+    def scores_step(self, pool, q_idx, w, stream=None):
+        L.dsa_indexer_scores(self.kv, pool, self.batch, q_idx, w, self.scores, self.hist, stream)
+
+    def topk_step(self, stream=None, phys=None):
+        L.dsa_topk(self.kv, self.batch, self.scores, self.hist, self.k, self.idx, self.count,
+                   phys, stream)
+
+    def attention_step(self, pool, q, stream=None):
+        fn = L.sparse_mla_prefill if self.prefill else L.sparse_mla_decode
+        fn(self.kv, pool, self.batch, q, self.idx, self.k, self.softmax_scale, self.out,
+           self.lse, self.workspace, stream)
+
+    def run(self, pool, q_idx, w, q, stream=None):
+        self.scores_step(pool, q_idx, w, stream)
+        self.topk_step(stream)
+        self.attention_step(pool, q, stream)
+        return self.out

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every symbol include/dsa.h declares, and its host-side
+validation and layout logic behave as documented (no GPU needed: nothing here launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_decode_amd as sad
+from sparse_attention_decode_amd import _lib as L
+from conftest import ROOT
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "dsa.h")) as f:
+        text = f.read()
+    return re.findall(r"DSA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 8
+    assert set(names) == set(L.EXPORTS)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_layout_rows_match_page_byte_counts():
+    # Page (KV cache footprint / A KV cache for three kinds of state): FP8 index key 132 B per
+    # token including its scale, MXFP4 key 68 B, FP8 latent 576 B.
+    kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    assert kv.ikey_scale_off - kv.ikey_off == 64 * 128
+    assert (kv.ikey_scale_off - kv.ikey_off) // 64 + 4 == 132
+    assert kv.latent_scale_off - kv.latent_off == 64 * 576
+    assert kv.row_bytes == 64 * (576 + 4 + 128 + 4) == 45568
+    kv4 = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_NVFP4, 10, 0.5)
+    assert (kv4.ikey_scale_off - kv4.ikey_off) // 64 + 128 // 32 == 68
+    assert kv4.latent_scale_off - kv4.latent_off == 64 * 288
+    assert kv4.row_bytes == 64 * (288 + 36 + 64 + 4) == 25088
+    assert abs(kv4.latent_tensor_scale - 0.5) < 1e-7
+    for k in (kv, kv4):
+        for off in (k.latent_off, k.latent_scale_off, k.ikey_off, k.ikey_scale_off):
+            assert off % 16 == 0
+        assert k.row_bytes % 256 == 0
+
+
+def test_layout_rejects_bad_arguments():
+    with pytest.raises(sad.DSAError) as e:
+        sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10, block_size=32)
+    assert e.value.status == L.DSA_ERR_UNSUPPORTED
+    with pytest.raises(sad.DSAError) as e:
+        sad.kv_layout(7, sad.LATENT_FP8, 10)
+    assert e.value.status == L.DSA_ERR_INVALID_ARG
+    with pytest.raises(sad.DSAError):
+        sad.kv_layout(sad.IKEY_FP8, sad.LATENT_NVFP4, 10, 0.0)
+
+
+def _fake_batch(**over):
+    b = L.Batch()
+    b.num_seqs, b.num_rows, b.max_rows_per_seq, b.max_blocks_per_seq = 1, 1, 1, 2
+    b.max_context = 100
+    b.block_table = b.seq_row_start = b.row_pos = 0x1000
+    for k, v in over.items():
+        setattr(b, k, v)
+    return b
+
+
+def test_entry_points_validate_before_launch():
+    lib = L.lib()
+    kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    pool = ctypes.c_void_p(0x100000)
+    p = ctypes.c_void_p(0x2000)
+    b = _fake_batch()
+    # null pool
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), None, ctypes.byref(b), p, p, p, 128, None,
+                                  None) == L.DSA_ERR_INVALID_ARG
+    assert b"pool" in lib.dsa_last_error()
+    # misaligned pool
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), ctypes.c_void_p(0x100010), ctypes.byref(b),
+                                  p, p, p, 128, None, None) == L.DSA_ERR_INVALID_ARG
+    # ld below max_context
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), pool, ctypes.byref(b), p, p, p, 64, None,
+                                  None) == L.DSA_ERR_INVALID_ARG
+    # block table too narrow for max_context
+    b2 = _fake_batch(max_context=200)
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), pool, ctypes.byref(b2), p, p, p, 256, None,
+                                  None) == L.DSA_ERR_INVALID_ARG
+    # k out of range
+    for k in (0, 2049):
+        assert lib.dsa_topk(ctypes.byref(kv), ctypes.byref(b), p, 128, None, k, p, p, None,
+                            None) == L.DSA_ERR_INVALID_ARG
+        assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b), p, p, k, 0.1, p,
+                                     None, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    # phys rows need the layout
+    assert lib.dsa_topk(None, ctypes.byref(b), p, 128, None, 16, p, p, p, None) == \
+        L.DSA_ERR_INVALID_ARG
+    # decode MLA with several splits needs its workspace
+    b3 = _fake_batch(num_rows=1)
+    need = lib.sparse_mla_workspace_bytes(1, 2048)
+    assert need > 0
+    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, 2048, 0.1, p,
+                                 None, None, 0, None) == L.DSA_ERR_WORKSPACE
+    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, 2048, 0.1, p,
+                                 None, p, need - 1, None) == L.DSA_ERR_WORKSPACE
+    # MXFP4 keys on the prefill path are not built
+    kv4 = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_FP8, 10)
+    b4 = _fake_batch(max_rows_per_seq=64, num_rows=64)
+    assert lib.dsa_indexer_scores(ctypes.byref(kv4), pool, ctypes.byref(b4), p, p, p, 128, None,
+                                  None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_status_string(L.DSA_ERR_WORKSPACE) == b"DSA_ERR_WORKSPACE"
