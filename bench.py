@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of one DSA layer step (indexer scores -> exact top-2048 -> sparse MLA) on one MI355X.
+
+Default workload: batched decode, 16 sequences x 1 query row, each with 131,072 cached tokens,
+FP8 index keys (132 B/token) and FP8 latents (576 B + 4 B scale per token) in 64-token paged
+blocks from one shuffled pool, 96 MLA heads, top-k 2048.  A step processes one batch of 16 rows;
+consecutive steps rotate over independent batches (separate pools) so the 277 MB key stream is
+read from HBM rather than from the 256 MB memory-side cache.  Inputs are resident in HBM before
+the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-graph]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode layer query-tokens/s + achieved HBM TB/s (fraction of peak)"
+PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step (byte model): keys of every visible
+    token once per sequence, latents (+scales) of the selected tokens, the queries, the output
+    and its log-sum-exp, and the block table.  Returns (total, indexer share)."""
+    import numpy as np
+    key_b = 132 if wl.ikey_fmt == 0 else 68
+    lat_b = 580 if wl.lat_fmt == 0 else 324
+    idx_bytes = 0
+    total = 0
+    for b in range(wl.num_seqs):
+        rows = wl.rows_of(b)
+        L = int(wl.row_pos[rows].max()) + 1
+        nblk = (L + 63) // 64
+        seq_idx = L * key_b + 4 * nblk + len(rows) * (32 * 128 + 32 * 4)
+        idx_bytes += seq_idx
+        total += seq_idx
+        for r in rows:
+            nsel = min(wl.k, int(wl.row_pos[r]) + 1)
+            total += nsel * lat_b + 96 * 576 * 2 + 96 * 512 * 2 + 96 * 4
+    return total, idx_bytes
+
+
+def indexer_flops(wl):
+    f = 0
+    for b in range(wl.num_seqs):
+        for r in wl.rows_of(b):
+            f += 2 * 32 * 128 * (int(wl.row_pos[r]) + 1)
+    return f
+
+
+def cpu_baseline(cfg: int, wl, budget_s: float = 20.0):
+    """The oracle, as it stands, on a bounded sample of the workload's rows (host cores)."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    done_rows, spent = 0, 0.0
+    sample = []
+    # rows spread over the batch; stop once the budget is used
+    order = list(range(wl.num_rows))
+    step = max(1, len(order) // 8)
+    picks = order[::step]
+    for r in picks:
+        b = int(wl.row_seq[r])
+        n = int(wl.row_pos[r]) + 1
+        keys, ks, lat, ls = synth.seq_tensors(wl, b, n)
+        qi, hw = synth.qidx(wl.seed, int(wl.row_id[r]), 1, wl.wq)
+        qm = synth.qmla(wl.seed, int(wl.row_id[r]), 1)
+        t0 = time.perf_counter()
+        oracle.dsa_rows(wl.ikey_fmt, wl.lat_fmt, wl.row_pos[[r]], qi, hw, qm, keys, ks, lat, ls,
+                        wl.lat_tensor_scale, wl.k, wl.softmax_scale)
+        spent += time.perf_counter() - t0
+        done_rows += 1
+        sample.append(r)
+        if spent >= budget_s:
+            break
+    return {"value": done_rows / spent, "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done_rows} of {wl.num_rows} rows of {wl.name} (rows {sample}), full "
+                      f"layer per row (scores in fp64+fp32, top-k sort, fp64 attention), "
+                      f"{spent:.1f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--replicas", type=int, default=0, help="independent batches (0: auto)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "design is described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_decode_amd as sad
+    import synth
+    import synth.device
+
+    cfg = args.config
+    reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4}[cfg]
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    wls, devs, layers = [], [], []
+    for rep in range(reps):
+        wl = synth.decode_config(cfg, replica=rep)
+        kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
+        d = synth.device.stage(wl, kv.as_dict())
+        batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
+                                d["max_rows_per_seq"], d["max_context"])
+        layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale,
+                             prefill=d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ)
+        wls.append(wl)
+        devs.append(d)
+        layers.append(layer)
+        log(f"[bench] staged replica {rep} of {wl.name}: pool {d['pool'].numel() / 2**30:.2f} GiB")
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    graphs = []
+    use_graph = not args.no_graph
+    if use_graph:
+        s = torch.cuda.Stream()
+        for layer, d in zip(layers, devs):
+            layer.run(d["pool"], d["q_idx"], d["w"], d["q"])  # eager reference first
+        torch.cuda.synchronize()
+        ref_out = [l.out.clone() for l in layers]
+        for layer, d in zip(layers, devs):
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga, stream=s):
+                layer.scores_step(d["pool"], d["q_idx"], d["w"])
+            with torch.cuda.graph(gb, stream=s):
+                layer.topk_step()
+                layer.attention_step(d["pool"], d["q"])
+            graphs.append((ga, gb))
+        for (ga, gb), layer, ref in zip(graphs, layers, ref_out):
+            ga.replay()
+            gb.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(layer.out, ref), "graph replay differs from eager run"
+
+    def step(i, ev=None):
+        j = i % reps
+        if ev is not None:
+            ev[0].record(stream)
+        if use_graph:
+            graphs[j][0].replay()
+        else:
+            layers[j].scores_step(devs[j]["pool"], devs[j]["q_idx"], devs[j]["w"])
+        if ev is not None:
+            ev[1].record(stream)
+        if use_graph:
+            graphs[j][1].replay()
+        else:
+            layers[j].topk_step()
+            layers[j].attention_step(devs[j]["pool"], devs[j]["q"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    idx_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    wl = wls[0]
+    rows = wl.num_rows
+    ms_step = 1e3 * elapsed / args.steps
+    value = rows * args.steps / elapsed
+    total_b, idx_b = algorithmic_bytes(wl)
+    layer_gbps = total_b / (ms_step * 1e-3) / 1e9
+    idx_gbps = idx_b / (idx_ms * 1e-3) / 1e9
+    flops = indexer_flops(wl)
+    prefill = cfg == 3
+    if prefill:
+        roof = {"bound": "mfma", "achieved": flops / (idx_ms * 1e-3) / 1e12,
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "indexer_decode_kernel (dsa_indexer_scores)"
+    roof["ms_per_launch"] = idx_ms
+    roof["algorithmic_bytes_per_launch"] = idx_b
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 (indexer) / bf16+fp16 (attention), fp32 accumulate",
+        "data": "synthetic (seeded, exact-grid FP8 keys)",
+        "config": {"workload": wl.name, "seqs": wl.num_seqs, "rows": rows,
+                   "context": int(wl.seq_len.max()), "top_k": wl.k,
+                   "index_keys": "fp8" if wl.ikey_fmt == 0 else "mxfp4",
+                   "latent": "fp8" if wl.lat_fmt == 0 else "nvfp4", "block": 64,
+                   "batches_rotated": reps, "hip_graph": use_graph},
+        "layer_hbm": {"algorithmic_bytes_per_step": total_b, "achieved_GBps": layer_gbps,
+                      "frac_of_8TBps": layer_gbps / PEAK_HBM_GBPS},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the oracle on a CPU sample ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

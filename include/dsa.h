@@ -124,10 +124,11 @@ DSA_API dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, i
  *   w      [num_rows][32] fp32 head weights
  *   scores [num_rows][ld_scores] fp32 output; entries [0, row_pos[r]] are written, the rest are
  *          left untouched.  ld_scores >= max_context.
- *   hist   [num_rows][DSA_HIST_BINS] uint32 output or NULL: histogram of the top 11 bits of each
- *          written score's order-preserving key, consumed by dsa_topk to skip one pass over the
- *          scores.  Only available on the decode path (max_rows_per_seq <= 8); must be NULL
- *          otherwise.
+ *   hist   [num_rows][DSA_HIST_BINS] uint32 in/out or NULL: counts of the top 11 bits of each
+ *          written score's order-preserving key are added to it; dsa_topk consumes it (saving a
+ *          pass over the scores) and returns it to zero.  It must be all zero on entry: allocate
+ *          it zeroed once, and clear it yourself if scores are computed without a dsa_topk call.
+ *          Only available on the decode path (max_rows_per_seq <= 8); must be NULL otherwise.
  * Decode and speculative decode (max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ) stream the index keys
  * once per sequence and score all of that sequence's rows from each key read.  Prefill chunks
  * (more rows per sequence; FP8 keys only) run as a dense FP8 matrix contraction of row tiles
@@ -139,20 +140,26 @@ DSA_API dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool,
                               const uint8_t* q_idx, const float* w, float* scores,
                               int64_t ld_scores, uint32_t* hist, void* stream);
 
+/* Workspace bytes dsa_topk needs for num_rows rows whose positions are below max_context. */
+DSA_API size_t dsa_topk_workspace_bytes(int32_t num_rows, int64_t max_context);
+
 /*
  * Step 2 — exact top-k per row (page: keep the 2,048 highest-scoring tokens).  Order: score
  * descending, token index ascending (a tie goes to the lower index); -0 equals +0.  NaN scores
  * are not supported.
- *   scores/ld_scores/hist as produced by step 1 (hist may be NULL: one more pass is then made)
- *   k in [1, DSA_MAX_TOPK]
+ *   scores/ld_scores/hist as produced by step 1 (hist may be NULL: the histogram is then built
+ *         here, one more pass over the scores).  A given hist is returned to zero.
+ *   k in [1, DSA_MAX_TOPK]; max_context up to 8,388,608
  *   idx   [num_rows][k] int32 output: the selected token indices in ascending order, then -1
  *   count [num_rows] int32 output: min(k, row_pos[r] + 1)
  *   phys  [num_rows][k] int32 output or NULL: physical pool rows (block * bs + slot) of idx,
  *         -1 padded (kv is required when phys is not NULL)
+ *   workspace: device scratch of at least dsa_topk_workspace_bytes(num_rows, max_context) bytes
  */
 DSA_API dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float* scores,
-                    int64_t ld_scores, const uint32_t* hist, int32_t k, int32_t* idx,
-                    int32_t* count, int32_t* phys, void* stream);
+                            int64_t ld_scores, uint32_t* hist, int32_t k, int32_t* idx,
+                            int32_t* count, int32_t* phys, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes sparse_mla_decode needs for num_rows rows and top-k k. */
 DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k);
@@ -165,19 +172,23 @@ DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k);
  *   logit_j = softmax_scale * q[r,h] . c_j ;  p = softmax(logit)
  *   out[r,h] = sum_j p_j c_j[0:512] ;  lse[r,h] = max + ln sum exp(logit - max)
  *   q    [num_rows][96][576] bf16;  idx [num_rows][k] from dsa_topk
+ *   phys [num_rows][k] pool rows of idx from dsa_topk, or NULL (then idx is translated through
+ *        the block table here).  Passing the rows the select already emitted saves a dependent
+ *        lookup per token (page: the select emits the physical KV rows the attention reads).
  *   out  [num_rows][96][512] bf16 output;  lse [num_rows][96] fp32 output or NULL
  *   workspace: device scratch of at least sparse_mla_workspace_bytes(num_rows, k) bytes
- * A row with no selected token gets out = 0 and lse = -inf.
+ * A row with no selected token gets out = 0 and lse = -inf.  Latent token scales (FP8) and the
+ * tensor scale (NVFP4) must be positive and below 4096 (they scale fp16 probabilities).
  * The decode variant splits each row's selected set over several workgroups and merges the
  * partial results by log-sum-exp; the prefill variant (for thousands of rows) gives each row one
  * workgroup across all heads and needs no workspace (it may be NULL).
  */
 DSA_API dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
-                             const uint16_t* q, const int32_t* idx, int32_t k,
+                             const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
                              float softmax_scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 DSA_API dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
-                              const uint16_t* q, const int32_t* idx, int32_t k,
+                              const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
                               float softmax_scale, uint16_t* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream);
 

@@ -16,7 +16,8 @@ INDEX_HEADS, INDEX_DIM, MLA_HEADS, MLA_DQK, MLA_DV = 32, 128, 96, 576, 512
 MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 
 # Every symbol include/dsa.h declares.
-EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk", "sparse_mla_workspace_bytes",
+EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
+           "sparse_mla_workspace_bytes",
            "sparse_mla_decode", "sparse_mla_prefill", "dsa_status_string", "dsa_last_error")
 
 
@@ -61,16 +62,18 @@ def lib():
         L.dsa_indexer_scores.restype = i32
         L.dsa_indexer_scores.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp,
                                          vp, vp, i64, vp, vp]
+        L.dsa_topk_workspace_bytes.restype = ctypes.c_size_t
+        L.dsa_topk_workspace_bytes.argtypes = [i32, i64]
         L.dsa_topk.restype = i32
         L.dsa_topk.argtypes = [ctypes.POINTER(KVLayout), ctypes.POINTER(Batch), vp, i64, vp, i32,
-                               vp, vp, vp, vp]
+                               vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sparse_mla_workspace_bytes.restype = ctypes.c_size_t
         L.sparse_mla_workspace_bytes.argtypes = [i32, i32]
         for fn in ("sparse_mla_decode", "sparse_mla_prefill"):
             f = getattr(L, fn)
             f.restype = i32
-            f.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp, vp, i32, f32,
-                          vp, vp, vp, ctypes.c_size_t, vp]
+            f.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp, vp, vp, i32,
+                          f32, vp, vp, vp, ctypes.c_size_t, vp]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [i32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -131,31 +134,36 @@ def dsa_indexer_scores(kv: KVLayout, pool, batch: DeviceBatch, q_idx, w, scores,
                                     _ptr(hist), _stream(stream)), "dsa_indexer_scores")
 
 
+def dsa_topk_workspace_bytes(num_rows: int, max_context: int) -> int:
+    return int(lib().dsa_topk_workspace_bytes(num_rows, max_context))
+
+
 def dsa_topk(kv: KVLayout | None, batch: DeviceBatch, scores, hist, k: int, idx, count,
-             phys=None, stream=None):
+             workspace, phys=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_topk(ctypes.byref(kv) if kv is not None else None, ctypes.byref(batch.c),
                           _ptr(scores), scores.stride(0), _ptr(hist), k, _ptr(idx), _ptr(count),
-                          _ptr(phys), _stream(stream)), "dsa_topk")
+                          _ptr(phys), _ptr(workspace), ws_bytes, _stream(stream)), "dsa_topk")
 
 
 def sparse_mla_workspace_bytes(num_rows: int, k: int) -> int:
     return int(lib().sparse_mla_workspace_bytes(num_rows, k))
 
 
-def _mla(fn: str, kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace, stream):
+def _mla(fn: str, kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, workspace, stream):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), fn)(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c), _ptr(q),
-                              _ptr(idx), k, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
-                              ws_bytes, _stream(stream)), fn)
+                              _ptr(idx), _ptr(phys), k, softmax_scale, _ptr(out), _ptr(lse),
+                              _ptr(workspace), ws_bytes, _stream(stream)), fn)
 
 
 def sparse_mla_decode(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None, workspace=None,
-                      stream=None):
-    _mla("sparse_mla_decode", kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
-         stream)
+                      stream=None, phys=None):
+    _mla("sparse_mla_decode", kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse,
+         workspace, stream)
 
 
 def sparse_mla_prefill(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None, workspace=None,
-                       stream=None):
-    _mla("sparse_mla_prefill", kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
-         stream)
+                       stream=None, phys=None):
+    _mla("sparse_mla_prefill", kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse,
+         workspace, stream)

@@ -12,21 +12,22 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *FLAGS, *["-D" + d for d in defines], *[os.path.join(CSRC, s) for s in SOURCES],
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines()
+    log = "\n".join(l for l in r.stdout.splitlines()
                     if "unknown target feature" not in l and "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("hipcc failed:\n" + log)
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

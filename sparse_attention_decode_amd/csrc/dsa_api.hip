@@ -73,6 +73,7 @@ dsa::PoolView pool_view(const dsa_kv_layout* kv, const void* pool) {
   p.lat_scale_off = kv->latent_scale_off;
   p.ikey_off = kv->ikey_off;
   p.ikey_scale_off = kv->ikey_scale_off;
+  p.tokens = kv->num_blocks * kv->block_size;
   return p;
 }
 
@@ -90,7 +91,8 @@ dsa::BatchView batch_view(const dsa_batch* b) {
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
-                      const uint16_t* q, const int32_t* idx, int32_t k, float softmax_scale,
+                      const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
+                      float softmax_scale,
                       uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, bool prefill) {
   dsa_status st = check_layout(kv, pool);
@@ -107,6 +109,7 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.batch = batch_view(batch);
   a.q = q;
   a.idx = idx;
+  a.phys = phys;
   a.k = k;
   a.softmax_scale = softmax_scale;
   a.tensor_scale = kv->latent_format == DSA_LATENT_NVFP4 ? kv->latent_tensor_scale : 1.f;
@@ -116,15 +119,18 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.tokens_per_split = (int32_t)align_up((k + a.nsplit - 1) / a.nsplit, 32);
   a.nsplit = (k + a.tokens_per_split - 1) / a.tokens_per_split;
   a.part_o = nullptr;
-  a.part_ml = nullptr;
+  a.part_lse = nullptr;
+  a.part_exp = nullptr;
   if (a.nsplit > 1) {
     const size_t need = dsa::mla_workspace_bytes(batch->num_rows, k);
     if (!workspace || workspace_bytes < need)
       return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = a.part_o + (size_t)batch->num_rows * a.nsplit * DSA_MLA_HEADS * DSA_MLA_DV;
+    const size_t nslot = (size_t)batch->num_rows * a.nsplit * DSA_MLA_HEADS;
+    a.part_o = static_cast<uint16_t*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(a.part_o + nslot * DSA_MLA_DV);
+    a.part_exp = reinterpret_cast<int32_t*>(a.part_lse + nslot);
   }
   return hip_status(dsa::launch_sparse_mla(a, kv->latent_format, stream),
                     prefill ? "sparse_mla_prefill launch" : "sparse_mla_decode launch");
@@ -213,9 +219,15 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
                     "prefill indexer launch");
 }
 
+size_t dsa_topk_workspace_bytes(int32_t num_rows, int64_t max_context) {
+  if (num_rows <= 0 || max_context <= 0) return 0;
+  return dsa::topk_workspace_bytes(num_rows, max_context);
+}
+
 dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float* scores,
-                    int64_t ld_scores, const uint32_t* hist, int32_t k, int32_t* idx,
-                    int32_t* count, int32_t* phys, void* stream) {
+                    int64_t ld_scores, uint32_t* hist, int32_t k, int32_t* idx,
+                    int32_t* count, int32_t* phys, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   g_err[0] = 0;
   dsa_status st = check_batch(batch);
   if (st != DSA_OK) return st;
@@ -223,21 +235,31 @@ dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
   if (ld_scores < batch->max_context)
     return fail(DSA_ERR_INVALID_ARG, "ld_scores %lld < max_context", (long long)ld_scores);
+  if (batch->max_context > (int64_t)dsa::kMaxSlices * dsa::kTopkSlice)
+    return fail(DSA_ERR_UNSUPPORTED, "top-k is built for contexts up to %d tokens",
+                dsa::kMaxSlices * dsa::kTopkSlice);
   if (phys) {
     if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is required for phys rows");
     if (kv->block_size != 64) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
   }
   if (batch->num_rows == 0) return DSA_OK;
-  dsa::TopkArgs a;
+  const size_t need = dsa::topk_workspace_bytes(batch->num_rows, batch->max_context);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
+  dsa::TopkArgs a = {};
   a.batch = batch_view(batch);
   a.scores = scores;
   a.ld = ld_scores;
-  a.hist = hist;
+  a.hist_in = hist;
   a.k = k;
   a.idx = idx;
   a.count = count;
   a.phys = phys;
-  return hip_status(dsa::launch_topk(a, static_cast<hipStream_t>(stream)), "topk launch");
+  return hip_status(dsa::launch_topk(a, batch->max_context, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                    "topk launch");
 }
 
 size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k) {
@@ -246,20 +268,20 @@ size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k) {
 }
 
 dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
-                             const uint16_t* q, const int32_t* idx, int32_t k,
+                             const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
                              float softmax_scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  return mla_common(kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+  return mla_common(kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream), false);
 }
 
 dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
-                              const uint16_t* q, const int32_t* idx, int32_t k,
+                              const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
                               float softmax_scale, uint16_t* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  return mla_common(kv, pool, batch, q, idx, k, softmax_scale, out, lse, workspace,
+  return mla_common(kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream), true);
 }
 

@@ -21,6 +21,7 @@ constexpr int kBlock = 64;  // tokens per pool block (the only block size built)
 struct PoolView {
   const uint8_t* base;
   int64_t row_bytes, lat_off, lat_scale_off, ikey_off, ikey_scale_off;
+  int64_t tokens;  // num_blocks * block size: bound on physical token rows
 };
 
 // Order-preserving 32-bit key of an fp32 score: a larger score gives a larger key; -0 maps to the

@@ -34,30 +34,42 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int64_t max_context,
                                   int32_t max_rows_per_seq, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 
+constexpr int kTopkSlice = 4096;   // scores per filter workgroup
+constexpr int kMaxSlices = 2048;   // => contexts up to 8M tokens
+
 struct TopkArgs {
   BatchView batch;
   const float* scores;
   int64_t ld;
-  const uint32_t* hist;  // or null
+  uint32_t* hist_in;  // [R][2048] key histogram (from the scorer or the hist pass); zeroed once consumed
   int32_t k;
   int32_t* idx;
   int32_t* count;
   int32_t* phys;  // or null
+  // workspace views (set by launch_topk)
+  uint32_t* slice_cnt;  // [R][num_slices] survivors per slice
+  uint2* cand;          // [R][cand_ld] survivors (order key, token index), slice-major
+  int64_t cand_ld;
+  int32_t num_slices;
+  int32_t vec_ok;       // scores rows are 16-byte aligned
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+size_t topk_workspace_bytes(int32_t num_rows, int64_t max_context);
+hipError_t launch_topk(const TopkArgs& a, int64_t max_context, void* workspace, hipStream_t s);
 
 struct MlaArgs {
   PoolView pool;
   BatchView batch;
   const uint16_t* q;  // [R][96][576] bf16
   const int32_t* idx; // [R][k]
+  const int32_t* phys; // [R][k] pool rows of idx, or null
   int32_t k;
   float softmax_scale;
   float tensor_scale;  // NVFP4 latent tensor scale (1 for FP8)
   uint16_t* out;       // [R][96][512] bf16
   float* lse;          // [R][96] or null
-  float* part_o;       // [R][nsplit][96][512] fp32 (split path)
-  float* part_ml;      // [R][nsplit][96][2] fp32 (split path)
+  uint16_t* part_o;    // [R][nsplit][96][512] fp16 normalised split outputs * 2^part_exp
+  float* part_lse;     // [R][nsplit][96] base-2 log-sum-exp of each split
+  int32_t* part_exp;   // [R][nsplit][96] power-of-two scale exponent of each split output
   int32_t nsplit;
   int32_t tokens_per_split;
 };

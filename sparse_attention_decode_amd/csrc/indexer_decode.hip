@@ -22,7 +22,13 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;         // 4 waves
-constexpr int kBlocksPerWave = 4;     // 64-token pages per wave per workgroup
+#ifndef DSA_IDX_PAGES_PER_WAVE
+#define DSA_IDX_PAGES_PER_WAVE 4
+#endif
+#ifndef DSA_IDX_DEPTH
+#define DSA_IDX_DEPTH 1
+#endif
+constexpr int kBlocksPerWave = DSA_IDX_PAGES_PER_WAVE;  // 64-token pages per wave per workgroup
 constexpr int kBlocksPerWG = kBlocksPerWave * (kThreads / kWave);
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
 
@@ -104,43 +110,79 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
   }
 
   const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
-  for (int ib = 0; ib < kBlocksPerWave; ++ib) {
-    const int blk = blk0 + ib * (kThreads / kWave) + wave;
-    if (blk >= nblk) break;
-    const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
-    KeyFrag f[4];
+  // Each wave walks its pages (blk0 + wave + 4i) as a software pipeline with D pages in flight:
+  // the operands of page i+D are loading while page i is scored.  Register slots rotate with the
+  // fully unrolled stage index, so every slot is a fixed register range.
+  constexpr int D = R <= 2 ? DSA_IDX_DEPTH : 1;
+  constexpr int S = D + 1;
+  constexpr int kWaves = kThreads / kWave;
+  auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
+  auto load_page = [&](KeyFrag* f, int i) {
+    const int blk = page_of(i);
+    if (i < kBlocksPerWave && blk < nblk) {
+      const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
+      for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
+    }
+  };
+  KeyFrag buf[S][4];
+  // Scores stay in registers until the wave's last page has been loaded: loads and stores share
+  // one completion counter, so a store issued between loads would make every later wait for key
+  // data also wait for that store's acknowledgement.
+  float sbuf[R][kBlocksPerWave];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int s = blk * kBlock + 16 * nt + c;  // token of this lane's column
+  for (int i = 0; i < D; ++i) load_page(buf[i], i);
+#pragma unroll
+  for (int base = 0; base < kBlocksPerWave; base += S) {
+    if (page_of(base) >= nblk) break;
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const int i = base + st;
+      load_page(buf[(st + D) % S], i + D);
+      const int blk = page_of(i);
+      if (i >= kBlocksPerWave || blk >= nblk) break;
+      const KeyFrag* cur = buf[st];
+      // After the cross-lane head sum every lane group holds the scores of all four 16-token
+      // tiles; lane group g keeps tile g's, so lane l holds the score of token 64*blk + l.
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (r >= nr) break;
-        v4f z = {0.f, 0.f, 0.f, 0.f};
-        v4f acc0, acc1;
-        if (KFMT == DSA_IKEY_FP8) {
-          acc0 = mfma_fp8(qa[r][0], f[nt].b, z);
-          acc1 = mfma_fp8(qa[r][1], f[nt].b, z);
-        } else {
-          acc0 = mfma_fp8_fp4(qa[r][0], f[nt].b, z, 127, f[nt].escale);
-          acc1 = mfma_fp8_fp4(qa[r][1], f[nt].b, z, 127, f[nt].escale);
-        }
-        float part = 0.f;
+        float mine = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          part += wv[r][0][i] * fmaxf(acc0[i], 0.f);
-          part += wv[r][1][i] * fmaxf(acc1[i], 0.f);
+        for (int nt = 0; nt < 4; ++nt) {
+          v4f z = {0.f, 0.f, 0.f, 0.f};
+          v4f acc0, acc1;
+          if (KFMT == DSA_IKEY_FP8) {
+            acc0 = mfma_fp8(qa[r][0], cur[nt].b, z);
+            acc1 = mfma_fp8(qa[r][1], cur[nt].b, z);
+          } else {
+            acc0 = mfma_fp8_fp4(qa[r][0], cur[nt].b, z, 127, cur[nt].escale);
+            acc1 = mfma_fp8_fp4(qa[r][1], cur[nt].b, z, 127, cur[nt].escale);
+          }
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part += wv[r][0][e] * fmaxf(acc0[e], 0.f);
+            part += wv[r][1][e] * fmaxf(acc1[e], 0.f);
+          }
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+          if (g == nt) mine = part * cur[nt].scale;
         }
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
-        const float score = part * f[nt].scale;
-        if (g == (r & 3) && s <= pos[r]) {
-          a.scores[(int64_t)(r0 + r) * a.ld + s] = score;
-          if (use_hist) atomicAdd(&s_hist[r * kBins + (order_key(score) >> 21)], 1u);
-        }
+        sbuf[r][i] = mine;
+        if (use_hist && blk * kBlock + lane <= pos[r])
+          atomicAdd(&s_hist[r * kBins + (order_key(mine) >> 21)], 1u);
       }
     }
+  }
+  // one coalesced 256-byte store per (page, row)
+#pragma unroll
+  for (int i = 0; i < kBlocksPerWave; ++i) {
+    const int s = page_of(i) * kBlock + lane;
+    if (page_of(i) >= nblk) break;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr && s <= pos[r]) a.scores[(int64_t)(r0 + r) * a.ld + s] = sbuf[r][i];
   }
 
   if (use_hist) {
@@ -190,10 +232,6 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
                                  int64_t max_context, hipStream_t s) {
   IndexerArgs a = a0;
   a.tiles_per_seq = 1;
-  if (a.hist) {
-    hipError_t e = launch_zero_u32(a.hist, (int64_t)a.batch.num_rows * kBins, s);
-    if (e != hipSuccess) return e;
-  }
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
   dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)a.batch.num_seqs);
   return ikey_fmt == DSA_IKEY_FP8 ? launch_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)

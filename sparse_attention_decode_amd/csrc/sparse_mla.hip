@@ -12,215 +12,407 @@
 //   logit_j = softmax_scale * q[r,h] . c_j      (576 dims; no positional encoding)
 //   out[r,h] = sum_j softmax(logit)_j * c_j[0:512]
 //
-// Design (gfx950): a workgroup of 6 waves takes one row (or one split of its selected set), wave w
-// owning heads [16w, 16w+16).  Tiles of 32 selected tokens are gathered from the paged pool, the
-// codes converted exactly and staged twice in LDS: token-major bf16 (A operand of S^T = C Q^T,
-// against the bf16 query) and dim-major fp16 (A operand of O^T = V^T P^T; the probabilities go
-// in as fp16, whose 11-bit significand keeps their rounding well inside the output tolerance).  Per-token scales stay out of the MFMA
-// operands: they multiply the logits and the probabilities.  With S^T and O^T the softmax
-// statistics of a head live in the same lane as that head's output column, and the probabilities
-// of S^T are already in B-operand position for PV (the K order of the PV contraction is permuted
-// to match), so no register shuffles or LDS round trips are needed between the two products.
-// Softmax is online (running max and sum per head, in base 2).
+// Design (gfx950).  A workgroup of 12 waves takes one row (or one split of its selected set).
+// Waves 2h and 2h+1 own heads [16h, 16h+16); wave 2h+d computes the half d of the QK contraction
+// (288 of the 576 dims) and the half d of the output dims (256 of 512), so a wave holds 36 query
+// registers and 64 accumulator registers, and three waves share each SIMD.  Tiles of 32 selected
+// tokens are gathered from the paged pool straight into LDS with direct global->LDS loads (no
+// registers held in flight), three stages deep so the gathers of tiles j+1 and j+2 overlap the
+// math of tile j.
+//   QK^T: S^T[tokens x heads] = C Q^T on bf16 MFMA.  The query stays in registers (B operand);
+//         the latent tile is the A operand.  FP8 latents are read raw from LDS and converted to
+//         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
+//         The two partial S^T of a wave pair are added through LDS (both waves then hold the
+//         same bits, so their softmax statistics agree exactly).
+//   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  V^T comes from a dim-major copy of the
+//         value dims (FP8 bytes, or fp16 for NVFP4); P^T is S^T's softmax, already in B-operand
+//         position: the K order of this contraction is permuted so that lane group g holds
+//         tokens {4g..4g+3, 16+4g..16+4g+3}, and the dim-major tile stores tokens in that order.
+// Per-token scales stay out of the MFMA operands (they multiply the logits and the
+// probabilities), so every operand is an exact conversion of the stored codes.  fp16 for P keeps
+// its rounding well inside the output tolerance.  Softmax is online, in base 2.  With S^T and
+// O^T a head's softmax statistics live in the same lane as that head's output column.
+// LDS rows are padded so that the MFMA operand reads are bank-conflict free.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kWavesM = DSA_MLA_HEADS / 16;  // 6
-constexpr int kThreadsM = kWavesM * kWave;    // 384
-constexpr int kTile = 32;                     // selected tokens per tile
-constexpr int kKSteps = DSA_MLA_DQK / 32;     // 18
-constexpr int kCtStride = DSA_MLA_DQK + 8;    // bf16 elements per token row (padded)
-constexpr int kVtStride = kTile + 4;          // bf16 elements per dim row (padded)
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWavesM = 2 * DSA_MLA_HEADS / 16;  // 12: 6 head groups x 2 halves
+constexpr int kThreadsM = kWavesM * kWave;        // 768
+constexpr int kTile = 32;                         // selected tokens per tile
+constexpr int kSteps = DSA_MLA_DQK / 32 / 2;      // 9 K steps of 32 dims per wave (half of 576)
+constexpr int kDvHalf = DSA_MLA_DV / 2;           // 256 output dims per wave
+constexpr int kPhysRing = 512;                // pool rows of upcoming selected tokens
+constexpr int kStages = 3;                    // gather pipeline: tiles j, j+1, j+2 in flight
+constexpr int kRowsPerWave = (kTile + kWavesM - 1) / kWavesM;  // 3 (rows >= 32 are dummies)
+// Every wave issues exactly this many gathers per tile (data + scale per row, dummies included),
+// so waiting for a tile is "all but the newest tile's gathers are done".
+constexpr int kGathersPerWave = 2 * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabilities <= 16)
 
-struct MlaShared {
-  uint16_t ct[kTile * kCtStride];          // [token][dim] bf16
-  uint16_t vt[DSA_MLA_DV * kVtStride];     // [dim][token] fp16
-  float tscale[kTile];                     // per-token scale (0 = no token)
-  int32_t valid[kTile];
+// FP8 latents
+constexpr int kRaw8 = 592;   // raw row bytes: 576 codes + pad (148 dwords: b128 reads conflict-free)
+constexpr int kVt8 = 40;     // dim-major row bytes: 32 tokens + pad (10 dwords)
+// NVFP4 latents
+constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
+constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords)
+constexpr int kVt4 = 80;     // fp16 dim-major row bytes: 64 + pad (20 dwords)
+
+template <int LFMT>
+struct Geo {
+  static constexpr bool kFp8 = LFMT == DSA_LATENT_FP8;
+  static constexpr int kRaw = kFp8 ? kRaw8 : kRaw4;
+  static constexpr int kVt = kFp8 ? kVt8 : kVt4;
+  static constexpr int kCtBytes = kFp8 ? 16 : kTile * kCt4;  // decoded tile (NVFP4 only)
 };
 
-// Store 16 latent values (exact fp32) of token t, dims d0..d0+15: bf16 into the token-major tile
-// (QK^T operand) and, for value dims, fp16 into the dim-major tile (PV operand).  Every FP8 and
-// NVFP4 latent value is exactly representable in both formats.
-__device__ __forceinline__ void store_dims(MlaShared& sh, int t, int d0, const float* v) {
-  uint32_t* crow = reinterpret_cast<uint32_t*>(&sh.ct[t * kCtStride + d0]);
+// One pipeline stage: where a gathered tile lands.  Each stage's buffers are separate
+// __shared__ variables, so the compiler can tell the reads of one stage from the gathers still
+// landing in the others (one shared array would make it wait for every gather before any read).
+struct Stage {
+  uint8_t* raw;    // [kTile][kRaw] latent rows as stored
+  float* tsc;      // [kTile] FP8 token scales
+  int32_t* valid;  // [kTile] slot holds a selected, visible token
+};
+
+// Workgroup barrier over LDS only: waits for this wave's LDS operations, not its global loads
+// (those are waited for explicitly, per stage).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Position of tile token t (quad q = t / 4, u = t % 4) in a dim-major row: the K slot that holds
+// it in the PV contraction.
+__device__ __forceinline__ int vt_pos(int t) {
+  const int q = t >> 2, u = t & 3;
+  return 8 * (q & 3) + 4 * (q >> 2) + u;
+}
+
+// Issue the direct global->LDS gathers of tile j (selected slots [j, min(j+32, jend))) into stage
+// st.  Wave w gathers tile rows w, w+12, w+24; rows past the tile and slots without a token
+// gather a harmless dummy (pool row 0) into `junk`, so that every wave issues kGathersPerWave
+// loads per tile.
+template <int LFMT>
+__device__ __forceinline__ void issue_tile(const Stage& st, const int32_t* phys, uint8_t* junk,
+                                           const MlaArgs& a, int j, int jend, int j0) {
+  using G = Geo<LFMT>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    crow[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
-  if (d0 < DSA_MLA_DV) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sh.vt[(d0 + i) * kVtStride + t] = (uint16_t)f16_bits(v[i]);
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int t = wave + kWavesM * r;
+    const int jj = j + t;
+    const int ph = __builtin_amdgcn_readfirstlane(
+        (t < kTile && jj < jend) ? phys[(jj - j0) % kPhysRing] : -1);  // wave-uniform
+    if (t < kTile && lane == 0) st.valid[t] = ph >= 0;
+    const uint8_t* row = a.pool.base + (int64_t)(ph >= 0 ? ph / kBlock : 0) * a.pool.row_bytes;
+    const int slot = ph >= 0 ? ph % kBlock : 0;
+    uint8_t* dst = t < kTile ? st.raw + t * G::kRaw : junk;
+    if constexpr (G::kFp8) {
+      float* dsc = t < kTile ? st.tsc + t : reinterpret_cast<float*>(junk + kRaw8);
+      if (lane < DSA_MLA_DQK / 16)
+        __builtin_amdgcn_global_load_lds(row + a.pool.lat_off + slot * DSA_MLA_DQK + 16 * lane,
+                                         (lds_void*)dst, 16, 0, 0);
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds(row + a.pool.lat_scale_off + slot * 4, (lds_void*)dsc,
+                                         4, 0, 0);
+    } else {
+      if (lane < DSA_MLA_DQK / 32)
+        __builtin_amdgcn_global_load_lds(row + a.pool.lat_off + slot * (DSA_MLA_DQK / 2) + 16 * lane,
+                                         (lds_void*)dst, 16, 0, 0);
+      if (lane < DSA_MLA_DQK / 64)
+        __builtin_amdgcn_global_load_lds(
+            row + a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16) + 4 * lane,
+            (lds_void*)(dst + DSA_MLA_DQK / 2), 4, 0, 0);
+    }
   }
 }
 
-// Gather one tile of selected latents into LDS.  FP8: 36 pieces of 16 dims per token.  NVFP4:
-// 36 pieces of 16 dims (8 packed bytes + one E4M3 block scale) per token.
-template <int LFMT>
-__device__ void stage_tile(MlaShared& sh, const MlaArgs& a, const int32_t* bt, const int32_t* idx,
-                           int j, int jend, int nvis) {
-  const int tid = threadIdx.x;
-  constexpr int kPieces = kTile * (DSA_MLA_DQK / 16);  // 1152
-  for (int q = tid; q < kPieces; q += kThreadsM) {
-    const int t = q / (DSA_MLA_DQK / 16), p = q % (DSA_MLA_DQK / 16);
-    const int jj = j + t;
-    const int s = jj < jend ? idx[jj] : -1;
-    float vals[16];
-    if (s >= 0 && s < nvis) {
-      const uint8_t* row = a.pool.base + (int64_t)bt[s / kBlock] * a.pool.row_bytes;
-      const int slot = s % kBlock;
-      if (LFMT == DSA_LATENT_FP8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + a.pool.lat_off +
-                                                        slot * DSA_MLA_DQK + 16 * p);
-        fp8x4_to_f32x4(v.x, vals);
-        fp8x4_to_f32x4(v.y, vals + 4);
-        fp8x4_to_f32x4(v.z, vals + 8);
-        fp8x4_to_f32x4(v.w, vals + 12);
-        if (p == 0) {
-          sh.tscale[t] = *reinterpret_cast<const float*>(row + a.pool.lat_scale_off + slot * 4);
-          sh.valid[t] = 1;
-        }
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(row + a.pool.lat_off +
-                                                        slot * (DSA_MLA_DQK / 2) + 8 * p);
-        const float bs = fp8_to_f32(row[a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16) + p]);
-        fp4x8_scaled_to_f32x8(v.x, bs, vals);
-        fp4x8_scaled_to_f32x8(v.y, bs, vals + 8);
-        if (p == 0) {
-          sh.tscale[t] = a.tensor_scale;
-          sh.valid[t] = 1;
-        }
-      }
+// FP8: dim-major copy of the value dims of a stage (bytes, transposed in 4x4 blocks); tokens that
+// are not selected get zeros so that their (zero) probabilities never meet stale data.
+__device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt) {
+  for (int blk = threadIdx.x; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
+    const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * tq + u;
+      w[u] = st.valid[t] ? *reinterpret_cast<const uint32_t*>(st.raw + t * kRaw8 + 4 * db) : 0u;
+    }
+    // 4x4 byte transpose with byte permutes: out[i] = {w0.byte i, w1.byte i, w2.byte i, w3.byte i}
+    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
+    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    const uint32_t v[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                           __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                           __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                           __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint32_t*>(vt + (4 * db + i) * kVt8 + vt_pos(4 * tq)) = v[i];
+  }
+}
+
+// NVFP4: decode a stage once into the bf16 token-major tile and the fp16 dim-major tile (E2M1 x
+// E4M3 products are exact in both).
+__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* vt) {
+  for (int it = threadIdx.x; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
+    const int t = it & 31, blk = it >> 5;  // token, 16-dim block
+    float v[16];
+    if (st.valid[t]) {
+      const uint2 p = *reinterpret_cast<const uint2*>(st.raw + t * kRaw4 + 8 * blk);
+      const float s = fp8_to_f32(st.raw[t * kRaw4 + DSA_MLA_DQK / 2 + blk]);
+      fp4x8_scaled_to_f32x8(p.x, s, v);
+      fp4x8_scaled_to_f32x8(p.y, s, v + 8);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vals[i] = 0.f;
-      if (p == 0) {
-        sh.tscale[t] = 0.f;
-        sh.valid[t] = 0;
-      }
+      for (int i = 0; i < 16; ++i) v[i] = 0.f;
     }
-    store_dims(sh, t, 16 * p, vals);
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+    uint4* crow = reinterpret_cast<uint4*>(ct + t * kCt4 + 32 * blk);
+    crow[0] = uint4{w[0], w[1], w[2], w[3]};
+    crow[1] = uint4{w[4], w[5], w[6], w[7]};
+    if (16 * blk < DSA_MLA_DV) {
+      const int pos = vt_pos(t);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *reinterpret_cast<uint16_t*>(vt + (16 * blk + i) * kVt4 + 2 * pos) = (uint16_t)f16_bits(v[i]);
+    }
+  }
+}
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const uint4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+  return __builtin_bit_cast(v8bf, r);
+}
+
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
+  const uint4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
+  return __builtin_bit_cast(v8h, r);
+}
+
+// K step i of contraction half dh: lane group g holds dims [288dh + 32i + 8g, +8).  The nine steps
+// of a half cover its 288 dims once; A and B operands use the same dims.
+constexpr int kHalfDims = DSA_MLA_DQK / 2;
+
+// Latent tile as the A operand of QK^T: token t, dims [d, d+8) (d = 288dh + 32i + 8g).
+template <int LFMT>
+__device__ __forceinline__ v8bf qk_operand(const Stage& st, const uint8_t* ct, int t, int d) {
+  if constexpr (LFMT == DSA_LATENT_FP8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(st.raw + t * kRaw8 + d);
+    return fp8x8_to_bf16(v.x, v.y);
+  } else {
+    return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(ct + t * kCt4 + 2 * d));
+  }
+}
+
+// Dim-major value tile as the A operand of PV: dim row d, lane group g (8 K slots).
+template <int LFMT>
+__device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int g) {
+  if constexpr (LFMT == DSA_LATENT_FP8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(vt + d * kVt8 + 8 * g);
+    return fp8x8_to_f16(v.x, v.y);
+  } else {
+    return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 16 * g));
   }
 }
 
 template <int LFMT>
 __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
-  __shared__ MlaShared sh;
-  const int row = blockIdx.x, split = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c = lane & 15;
-  const int head = 16 * wave + c;  // this lane's head in S^T / O^T columns
+  using G = Geo<LFMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[kTile * G::kRaw];
+  __shared__ __attribute__((aligned(16))) uint8_t raw1[kTile * G::kRaw];
+  __shared__ __attribute__((aligned(16))) uint8_t raw2[kTile * G::kRaw];
+  __shared__ float tsc0[kTile], tsc1[kTile], tsc2[kTile];
+  __shared__ int32_t valid0[kTile], valid1[kTile], valid2[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
+  __shared__ __attribute__((aligned(16))) v4f sx[kWavesM][2][kWave];  // partial S^T exchange
+  __shared__ float amx[kWavesM][16];
+  __shared__ int32_t phys[kPhysRing];
+  __shared__ __attribute__((aligned(16))) uint8_t junk[G::kRaw + 16];  // dummy gathers land here
+  static_assert(kStages == 3, "three stage variables");
+  const Stage stages[kStages] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2}};
 
-  // sequence of the row
-  int seq;
-  {
-    int lo = 0, hi = a.batch.num_seqs - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (a.batch.seq_row_start[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    seq = lo;
-  }
-  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
+  const int row = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave math scalar
+  const int g = lane >> 4, c = lane & 15;
+  const int dh = wave & 1;                // half of the QK dims and of the output dims
+  const int head = 16 * (wave >> 1) + c;  // this lane's head in S^T / O^T columns
+
   const int32_t* idx = a.idx + (int64_t)row * a.k;
+  const int32_t* prow = a.phys ? a.phys + (int64_t)row * a.k : nullptr;
   const int nvis = a.batch.row_pos[row] + 1;  // selected indices outside [0, nvis) are ignored
   const int j0 = split * a.tokens_per_split;
   const int j1 = min(a.k, j0 + a.tokens_per_split);
-
-  // Q^T fragments (B operand): lane holds head 16w+c, dims 32ks + 8g .. + 8
-  v8bf qf[kKSteps];
-  {
-    const uint16_t* qr = a.q + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DQK;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * g);
-      qf[ks] = __builtin_bit_cast(v8bf, v);
+  const int32_t* bt = nullptr;
+  if (!prow) {  // sequence of the row, by one ballot per 64 sequences
+    int seq = 0;
+    for (int b0 = 0; b0 < a.batch.num_seqs; b0 += kWave) {
+      const int b = b0 + lane;
+      const bool ended = b < a.batch.num_seqs && a.batch.seq_row_start[b + 1] <= row;
+      seq += __popcll(__ballot(ended));
     }
+    bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   }
-  v4f o[DSA_MLA_DV / 16];
+
+  // Pool rows of the selected tokens, kept kPhysRing/2 .. kPhysRing slots ahead of the tile being
+  // gathered: [j0, j0 + kPhysRing) now, then every kPhysRing/2 slots the next half.
+  auto fill_phys = [&](int from, int to) {
+    for (int jj = from + tid; jj < min(to, j1); jj += kThreadsM) {
+      int ph;
+      if (prow) {
+        ph = prow[jj];
+        if (ph >= a.pool.tokens) ph = -1;
+      } else {
+        const int s = idx[jj];
+        ph = (s >= 0 && s < nvis) ? bt[s / kBlock] * kBlock + (s % kBlock) : -1;
+      }
+      phys[(jj - j0) % kPhysRing] = ph;
+    }
+  };
+
+  // Q^T fragments (B operand) of this wave's half of the contraction
+  const int kd = kHalfDims * dh;  // first dim of the half (wave-uniform)
+  v8bf qf[kSteps];
+  {
+    const uint16_t* qr = a.q + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DQK + kd + 8 * g;
 #pragma unroll
-  for (int mt = 0; mt < DSA_MLA_DV / 16; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kSteps; ++i)
+      qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 32 * i));
+  }
+  fill_phys(j0, j0 + kPhysRing);
+  // Consume the query registers before any gather is issued: the compiler's wait for them is then
+  // a wait for loads that are done anyway, not a full wait inside the loop.
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) asm volatile("" ::"v"(qf[i]));
+  lds_barrier();
+  issue_tile<LFMT>(stages[0], phys, junk, a, j0, j1, j0);
+  issue_tile<LFMT>(stages[1], phys, junk, a, j0 + kTile, j1, j0);
+
+  v4f o[kDvHalf / 16];
+#pragma unroll
+  for (int mt = 0; mt < kDvHalf / 16; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = a.softmax_scale * kLog2e;
 
-  for (int j = j0; j < j1; j += kTile) {
-    __syncthreads();
-    stage_tile<LFMT>(sh, a, bt, idx, j, j1, nvis);
-    __syncthreads();
+  for (int jb = j0; jb < j1; jb += kStages * kTile) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {  // unrolled: stage s is a compile-time choice
+      const int j = jb + s * kTile;
+      if (j >= j1) break;
+      const Stage& cur = stages[s];
+      // all but the newest tile's gathers are done: tile j has landed (this wave's part)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGathersPerWave) : "memory");
+      lds_barrier();  // everyone's part landed; the previous tile's readers are done
+      if ((j - j0) % (kPhysRing / 2) == 0 && j > j0)
+        fill_phys(j + kPhysRing / 2, j + kPhysRing);  // overwrites slots already gathered
+      if constexpr (G::kFp8)
+        build_fp8(cur, vt);
+      else
+        build_nvfp4(cur, ct, vt);
+      issue_tile<LFMT>(stages[(s + 2) % kStages], phys, junk, a, j + 2 * kTile, j1, j0);
+      if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
-    // S^T (tokens x heads) for the two 16-token halves of the tile
-    v4f st[2];
+      // this wave's half of S^T (tokens x heads) for the two 16-token halves of the tile
+      v4f sfr[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = &sh.ct[(16 * h2 + c) * kCtStride + 8 * g];
+      for (int h2 = 0; h2 < 2; ++h2) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const uint4 v = *reinterpret_cast<const uint4*>(arow + 32 * ks);
-        acc = mfma_bf16(__builtin_bit_cast(v8bf, v), qf[ks], acc);
+        for (int i = 0; i < kSteps; ++i)
+          acc = mfma_bf16(qk_operand<LFMT>(cur, ct, 16 * h2 + c, kd + 32 * i + 8 * g), qf[i], acc);
+        sfr[h2] = acc;
+        sx[wave][h2][lane] = acc;
       }
-      st[h2] = acc;
-    }
-    // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head
-    float x[2][4];
-    float tmax = -INFINITY;
+      lds_barrier();  // partial S^T of both halves, and the value tile, are in LDS
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * h2 + 4 * g + i;
-        const float v = sh.valid[t] ? st[h2][i] * sh.tscale[t] * qk_scale : -INFINITY;
-        x[h2][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    uint32_t pb[4];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * h2 + 4 * g + i;
-        const float p = (x[h2][i] == -INFINITY) ? 0.f : exp2f(x[h2][i] - m_new);
-        psum += p;
-        pv[i] = p * sh.tscale[t];  // the token scale of c_j multiplies its value row
-      }
-      // fp16 pairs (round to nearest even): K slots 8g + 4*h2 + i  <->  token 16*h2 + 4g + i
-#pragma unroll
-      for (int i = 0; i < 2; ++i) pb[2 * h2 + i] = f16_bits(pv[2 * i]) | (f16_bits(pv[2 * i + 1]) << 16);
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const v8h pfrag = __builtin_bit_cast(v8h, uint4{pb[0], pb[1], pb[2], pb[3]});
+      for (int h2 = 0; h2 < 2; ++h2) sfr[h2] += sx[wave ^ 1][h2][lane];
 
-    // O^T (dims x heads) += V^T P^T; A operand lane: dim 16mt + c, tokens {4g..4g+3, 16+4g..}
+      // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head
+      float x[2][4], ts[2][4];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < DSA_MLA_DV / 16; ++mt) {
-      o[mt] *= alpha;
-      const uint16_t* vrow = &sh.vt[(16 * mt + c) * kVtStride];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-      const v8h af = __builtin_bit_cast(v8h, uint4{lo.x, lo.y, hi.x, hi.y});
-      o[mt] = mfma_f16(af, pfrag, o[mt]);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * h2 + 4 * g + i;
+          const bool ok = cur.valid[t];
+          // stale LDS bits of slots without a token are never used
+          const float scl = ok ? (G::kFp8 ? cur.tsc[t] : a.tensor_scale) : 0.f;
+          ts[h2][i] = scl;
+          const float v = ok ? sfr[h2][i] * scl * qk_scale : -INFINITY;
+          x[h2][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // Lazy rescaling: the running max only moves when a logit exceeds it by more than 2^4, so
+      // probabilities stay <= 16 and O is rarely rescaled.  The fp16 probability times the token
+      // scale must stay finite: token (or tensor) scales below 4096.
+      const float m_new = (tmax > m_run + kLazyMax) ? tmax : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      uint32_t pb[4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (x[h2][i] == -INFINITY) ? 0.f : exp2f(x[h2][i] - m_new);
+          psum += p;
+          pv[i] = p * ts[h2][i];  // the token scale of c_j multiplies its value row
+        }
+        // K slots 8g + 4*h2 + i  <->  token 16*h2 + 4g + i
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          pb[2 * h2 + i] = f16_bits(pv[2 * i]) | (f16_bits(pv[2 * i + 1]) << 16);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const v8h pfrag = __builtin_bit_cast(v8h, uint4{pb[0], pb[1], pb[2], pb[3]});
+      if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) {  // wave-uniform, rarely taken
+#pragma unroll
+        for (int mt = 0; mt < kDvHalf / 16; ++mt) o[mt] *= alpha;
+      }
+
+      // O^T (dims x heads) += V^T P^T; A operand lane: dim 256dh + 16mt + c, K slots 8g .. 8g+7
+#pragma unroll
+      for (int mt = 0; mt < kDvHalf / 16; ++mt)
+        o[mt] = mfma_f16(pv_operand<LFMT>(vt, kDvHalf * dh + 16 * mt + c, g), pfrag, o[mt]);
     }
   }
 
-  // lane holds O^T[16mt + 4g + i][head]
+  // the gathers issued ahead of the last tiles (dummies) land before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane holds O^T[256dh + 16mt + 4g + i][head]
+  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   if (a.nsplit == 1) {
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV;
+    uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + kDvHalf * dh;
 #pragma unroll
-    for (int mt = 0; mt < DSA_MLA_DV / 16; ++mt) {
+    for (int mt = 0; mt < kDvHalf / 16; ++mt) {
       uint32_t b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -229,54 +421,92 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       }
       *reinterpret_cast<uint2*>(orow + 16 * mt + 4 * g) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
     }
-    if (a.lse && g == 0)
+    if (a.lse && g == 0 && dh == 0)
       a.lse[(int64_t)row * DSA_MLA_HEADS + head] =
           (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
+    // Split partial: this split's normalised output as fp16 scaled by a power of two chosen from
+    // the head's largest value in the split (11 significant bits relative to that value, for any
+    // latent scale), the scale's exponent, and the split's base-2 log-sum-exp.
     const int64_t slot = ((int64_t)row * a.nsplit + split) * DSA_MLA_HEADS + head;
-    float* po = a.part_o + slot * DSA_MLA_DV;
+    float amax = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < DSA_MLA_DV / 16; ++mt)
-      *reinterpret_cast<float4*>(po + 16 * mt + 4 * g) =
-          float4{o[mt][0], o[mt][1], o[mt][2], o[mt][3]};
-    if (g == 0) {
-      a.part_ml[2 * slot] = m_run;
-      a.part_ml[2 * slot + 1] = l_run;
+    for (int mt = 0; mt < kDvHalf / 16; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[mt][i] * inv));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (g == 0) amx[wave][c] = amax;
+    lds_barrier();
+    amax = fmaxf(amax, amx[wave ^ 1][c]);  // over all 512 dims of the head
+    // 2^e * amax lies in [2^14, 2^15): well inside fp16's range and above its subnormals
+    const int e = (amax > 0.f) ? 14 - ilogbf(amax) : 0;
+    const float sc = inv * ldexpf(1.f, e);
+    uint16_t* po = a.part_o + slot * DSA_MLA_DV + kDvHalf * dh;
+#pragma unroll
+    for (int mt = 0; mt < kDvHalf / 16; ++mt)
+      *reinterpret_cast<uint2*>(po + 16 * mt + 4 * g) =
+          uint2{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
+                f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
+    if (g == 0 && dh == 0) {
+      a.part_lse[slot] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
+      a.part_exp[slot] = e;
     }
   }
 }
 
-// Merge the splits of each row by log-sum-exp.  grid (rows, 96 heads / 2); 256 threads: two heads,
+// Merge the splits of each row by log-sum-exp: out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
+// with o_s the split's normalised output.  grid (rows, 96 heads / 2); 256 threads: two heads,
 // 128 threads x 4 dims each.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int row = blockIdx.x;
   const int head = 2 * blockIdx.y + (threadIdx.x >> 7);
   const int d = 4 * (threadIdx.x & 127);
   const int64_t base = (int64_t)row * a.nsplit * DSA_MLA_HEADS + head;
+  // splits in groups of 8 with every load of a group issued before it is used
+  constexpr int G = 8;
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * DSA_MLA_HEADS)]);
+  for (int s0 = 0; s0 < a.nsplit; s0 += G) {
+    float ls[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      ls[u] = s0 + u < a.nsplit ? a.part_lse[base + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < G; ++u) M = fmaxf(M, ls[u]);
+  }
   float L = 0.f;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const int64_t slot = base + (int64_t)s * DSA_MLA_HEADS;
-      const float m = a.part_ml[2 * slot], l = a.part_ml[2 * slot + 1];
-      if (m == -INFINITY) continue;
-      const float wgt = exp2f(m - M);
-      L += wgt * l;
-      const float4 v = *reinterpret_cast<const float4*>(a.part_o + slot * DSA_MLA_DV + d);
-      acc.x += wgt * v.x;
-      acc.y += wgt * v.y;
-      acc.z += wgt * v.z;
-      acc.w += wgt * v.w;
+    for (int s0 = 0; s0 < a.nsplit; s0 += G) {
+      float ls[G];
+      int ex[G];
+      uint2 v[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int64_t slot = base + (int64_t)(s0 + u) * DSA_MLA_HEADS;
+        const bool in = s0 + u < a.nsplit;
+        ls[u] = in ? a.part_lse[slot] : -INFINITY;
+        ex[u] = in ? a.part_exp[slot] : 0;
+        v[u] = in ? *reinterpret_cast<const uint2*>(a.part_o + slot * DSA_MLA_DV + d) : uint2{0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (ls[u] == -INFINITY) continue;
+        const float wgt = exp2f(ls[u] - M);
+        L += wgt;
+        const float w2 = ldexpf(wgt, -ex[u]);
+        acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
+        acc[1] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16));
+        acc[2] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu));
+        acc[3] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16));
+      }
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  const float f[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   uint32_t b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t u = __float_as_uint(f[i]);
+    uint32_t u = __float_as_uint(acc[i] * inv);
     b[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   }
   *reinterpret_cast<uint2*>(a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + d) =
@@ -287,9 +517,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
 
 }  // namespace
 
+#ifndef DSA_MLA_TARGET_WGS
+#define DSA_MLA_TARGET_WGS 256
+#endif
 int mla_num_splits(int32_t num_rows, int32_t k) {
   const int tiles = (k + kTile - 1) / kTile;
-  int want = (256 + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
+  int want = (DSA_MLA_TARGET_WGS + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   return want;
@@ -298,11 +531,10 @@ int mla_num_splits(int32_t num_rows, int32_t k) {
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k) {
   const int ns = mla_num_splits(num_rows, k);
   if (ns <= 1) return 0;
-  return (size_t)num_rows * ns * DSA_MLA_HEADS * (DSA_MLA_DV + 2) * sizeof(float);
+  return (size_t)num_rows * ns * DSA_MLA_HEADS * (DSA_MLA_DV * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
-hipError_t launch_sparse_mla(const MlaArgs& a0, int lat_fmt, hipStream_t s) {
-  MlaArgs a = a0;
+hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
   if (a.batch.num_rows <= 0) return hipSuccess;
   dim3 grid((unsigned)a.batch.num_rows, (unsigned)a.nsplit);
   if (lat_fmt == DSA_LATENT_FP8)

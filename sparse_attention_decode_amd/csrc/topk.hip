@@ -6,231 +6,301 @@
 // Communication (a consistent tie rule).  Tie rule used here: the lower token index wins; -0 and
 // +0 tie.
 //
-// Per row, one 1024-thread workgroup:
-//   1. 11-bit radix histogram of the order-preserving keys (given by the scorer, or one pass);
-//   2. the bin holding the k-th largest key; its members are compacted into LDS and refined by
-//      two more radix levels (11 + 10 bits) to the exact k-th key T and the number E of keys
-//      equal to T that make the cut (falling back to passes over global memory when the bin does
-//      not fit in LDS);
-//   3. one ordered pass: a token is selected if key > T, or key == T and fewer than E keys equal
-//      to T precede it.  A block-wide prefix sum in token order gives each selected token its
-//      output slot, so the output comes out in ascending token order with no sort.
+// Keys: the order-preserving 32-bit image of each fp32 score.  Three kernels per call:
+//   hist    (only when the scorer did not provide it) 11-bit radix histogram of each row's keys;
+//   filter  many workgroups per row: each derives the threshold bin b1 (the 11-bit bin holding
+//           the k-th largest key) from the histogram, streams one slice of the row's scores and
+//           compacts the tokens whose key lies in a bin >= b1, in token order;
+//   resolve one workgroup per row: gathers the survivors (k plus the members of bin b1, a few
+//           thousand for long rows), refines bin b1 by two more radix levels (11 + 10 bits) to the
+//           exact k-th key T and the number E of keys equal to T that make the cut, then selects
+//           key > T, or key == T among the first E in token order.  A block prefix sum in token
+//           order places each selected token, so the output is ascending with no sort.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kBins = DSA_HIST_BINS;
-constexpr int kCap = 6144;  // LDS candidates of the threshold bin
+constexpr int kFilterThreads = 256;
+constexpr int kPerThread = kTopkSlice / kFilterThreads;  // 16 scores per thread
+constexpr int kHistChunk = 32768;                          // tokens per histogram workgroup
+constexpr int kResolveThreads = 1024;
+constexpr int kResolveWaves = kResolveThreads / kWave;
+constexpr int kCap = 8192;  // survivors resolved in LDS
 
-struct TopkShared {
-  uint32_t hist[kBins];
-  uint32_t cand_key[kCap];
-  int32_t cand_idx[kCap];
-  uint32_t wave_tot[kWaves];
-  uint32_t bcast[4];
-};
+__device__ __forceinline__ int row_seq(const BatchView& b, int row) {
+  int lo = 0, hi = b.num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (b.seq_row_start[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
-// Block-wide exclusive prefix sum of v in thread order; *total gets the sum over the block.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, TopkShared& sh) {
+// Block-wide exclusive prefix sum in thread order; *total receives the block sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* wtot) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) sh.wave_tot[wave] = incl;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  uint32_t wsum = 0, all = 0;
+  uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    uint32_t t = sh.wave_tot[i];
-    wsum += (i < wave) ? t : 0u;
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t t = wtot[i];
+    before += (i < wave) ? t : 0u;
     all += t;
   }
   __syncthreads();
   *total = all;
-  return wsum + incl - v;
+  return before + incl - v;
 }
 
-// Given a histogram of nbins bins (bin index increasing with the key), find the bin b holding the
-// need-th largest element: above(b) < need <= above(b) + hist[b].  Returns b and, in *need_in_bin,
-// need - above(b).  Every thread gets the result.
-__device__ uint32_t select_bin(TopkShared& sh, int nbins, uint32_t need, uint32_t* need_in_bin) {
+// Find the bin b of an nbins-bin histogram (bin index increasing with the key) that holds the
+// need-th largest element: above(b) < need <= above(b) + hist[b].  Returns b; *rest = need -
+// above(b).  hist is in LDS; every thread gets the result.  sc: LDS scratch of NT + 4 words.
+template <int NT>
+__device__ uint32_t select_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* rest,
+                               uint32_t* sc, uint32_t* wtot) {
   const int tid = threadIdx.x;
-  const int per = nbins / kThreads;  // 1 or 2 bins per thread
-  // thread t owns bins [per*t, per*t + per); count elements in bins owned by higher threads
+  const int per = nbins / NT;  // bins per thread (>= 1)
   uint32_t own = 0;
-  for (int j = 0; j < per; ++j) own += sh.hist[per * tid + j];
-  // exclusive scan in reverse thread order
-  const int rt = kThreads - 1 - tid;
+  for (int j = 0; j < per; ++j) own += hist[per * tid + j];
+  // suffix sums: scan the per-thread totals in reverse thread order
+  const int rt = NT - 1 - tid;
+  sc[rt] = own;
+  __syncthreads();
+  const uint32_t mine = sc[tid];
+  __syncthreads();
   uint32_t total;
-  // reverse order: do the scan on a permuted index by exchanging through LDS
-  __shared__ uint32_t tmp[kThreads];
-  tmp[rt] = own;
+  const uint32_t ex = block_excl_scan<NT>(mine, &total, wtot);
+  sc[tid] = ex;
   __syncthreads();
-  uint32_t mine = tmp[tid];  // value of thread (kThreads-1-tid)
-  __syncthreads();
-  uint32_t ex = block_excl_scan(mine, &total, sh);  // sum over threads with larger index than rt
-  tmp[tid] = ex;
-  __syncthreads();
-  uint32_t above = tmp[rt];  // elements in bins of threads > tid
+  uint32_t above = sc[rt];  // elements in bins owned by threads after this one
   __syncthreads();
   for (int j = per - 1; j >= 0; --j) {
     const int b = per * tid + j;
-    const uint32_t h = sh.hist[b];
+    const uint32_t h = hist[b];
     if (h && above < need && need <= above + h) {
-      sh.bcast[0] = (uint32_t)b;
-      sh.bcast[1] = need - above;
+      sc[NT] = (uint32_t)b;
+      sc[NT + 1] = need - above;
     }
     above += h;
   }
   __syncthreads();
-  uint32_t b = sh.bcast[0];
-  *need_in_bin = sh.bcast[1];
+  const uint32_t b = sc[NT];
+  *rest = sc[NT + 1];
   __syncthreads();
   return b;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-  __shared__ TopkShared sh;
+// ------------------------------------------------------------------ histogram (optional pass)
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t* hist) {
+  __shared__ uint32_t h[kBins];
+  const int row = blockIdx.y;
+  const int n = a.batch.row_pos[row] + 1;
+  if (n <= a.k) return;
+  const int s0 = blockIdx.x * kHistChunk;
+  if (s0 >= n) return;
+  const int s1 = min(n, s0 + kHistChunk);
+  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+  __syncthreads();
+  const float* sc = a.scores + (int64_t)row * a.ld;
+  for (int s = s0 + threadIdx.x * 4; s < s1; s += 256 * 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s + j < s1) atomicAdd(&h[order_key(sc[s + j]) >> 21], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += 256)
+    if (h[i]) atomicAdd(&hist[(int64_t)row * kBins + i], h[i]);
+}
+
+// ------------------------------------------------------------------ filter
+__global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sc[kFilterThreads + 4];
+  __shared__ uint32_t wtot[kFilterThreads / kWave];
+  const int row = blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = a.batch.row_pos[row] + 1;
+  const int base = slice * kTopkSlice;
+  if (n <= a.k || base >= n) return;
+
+  // issue the slice loads first; they overlap the threshold search below
+  const float* src = a.scores + (int64_t)row * a.ld + base + kPerThread * tid;
+  const int avail = n - base - kPerThread * tid;  // valid scores of this thread's run
+  float v[kPerThread];
+  if (avail >= kPerThread && a.vec_ok) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; j += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(src + j);
+      v[j] = f.x; v[j + 1] = f.y; v[j + 2] = f.z; v[j + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) v[j] = (j < avail) ? src[j] : 0.f;
+  }
+
+  const uint32_t* gh = a.hist_in + (int64_t)row * kBins;
+  for (int i = tid; i < kBins; i += kFilterThreads) hist[i] = gh[i];
+  __syncthreads();
+  uint32_t rest;
+  const uint32_t b1 = select_bin<kFilterThreads>(hist, kBins, (uint32_t)a.k, &rest, sc, wtot);
+
+  uint32_t mask = 0, cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const bool keep = j < avail && (order_key(v[j]) >> 21) >= b1;
+    mask |= keep ? (1u << j) : 0u;
+    cnt += keep ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t pos = block_excl_scan<kFilterThreads>(cnt, &total, wtot);
+  uint2* out = a.cand + (int64_t)row * a.cand_ld + base;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (mask & (1u << j)) out[pos++] = uint2{order_key(v[j]), (uint32_t)(base + kPerThread * tid + j)};
+  if (tid == 0) a.slice_cnt[(int64_t)row * a.num_slices + slice] = total;
+}
+
+// ------------------------------------------------------------------ resolve
+struct ResolveShared {
+  uint32_t hist[kBins];
+  uint32_t key[kCap];
+  int32_t idx[kCap];
+  uint32_t pre[kMaxSlices + 1];  // exclusive prefix of slice counts
+  uint32_t sc[kResolveThreads + 4];
+  uint32_t wtot[kResolveWaves];
+};
+
+__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs a) {
+  __shared__ ResolveShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = a.k;
   const int n = a.batch.row_pos[row] + 1;
   int32_t* out = a.idx + (int64_t)row * k;
   int32_t* phys = a.phys ? a.phys + (int64_t)row * k : nullptr;
-
-  // sequence of this row (rows are grouped by sequence)
-  if (tid == 0) {
-    int lo = 0, hi = a.batch.num_seqs - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (a.batch.seq_row_start[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    sh.bcast[2] = (uint32_t)lo;
-  }
-  __syncthreads();
-  const int seq = (int)sh.bcast[2];
-  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
+  const int32_t* bt = a.batch.block_table + (int64_t)row_seq(a.batch, row) * a.batch.ld_bt;
   auto phys_of = [&](int s) { return bt[s / kBlock] * kBlock + (s % kBlock); };
 
-  if (n <= k) {  // everything visible is selected
-    for (int i = tid; i < k; i += kThreads) {
+  uint32_t* hist_row = a.hist_in + (int64_t)row * kBins;
+  if (n <= k) {  // every visible token is selected
+    for (int i = tid; i < k; i += kResolveThreads) {
       out[i] = i < n ? i : -1;
       if (phys) phys[i] = i < n ? phys_of(i) : -1;
     }
+    for (int i = tid; i < kBins; i += kResolveThreads) hist_row[i] = 0;  // consumed
     if (tid == 0) a.count[row] = n;
     return;
   }
-  const float* sc = a.scores + (int64_t)row * a.ld;
+  const int nsl = (n + kTopkSlice - 1) / kTopkSlice;
 
-  // ---- level 1: histogram of key bits [31:21]
-  if (a.hist) {
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = a.hist[(int64_t)row * kBins + i];
-  } else {
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0;
+  // survivors per slice -> exclusive prefix
+  {
+    const uint32_t* cnt = a.slice_cnt + (int64_t)row * a.num_slices;
+    uint32_t carry = 0;
+    for (int s0 = 0; s0 < nsl; s0 += kResolveThreads) {
+      const uint32_t c = (s0 + tid < nsl) ? cnt[s0 + tid] : 0u;
+      uint32_t total;
+      const uint32_t ex = block_excl_scan<kResolveThreads>(c, &total, sh.wtot);
+      if (s0 + tid < nsl) sh.pre[s0 + tid] = carry + ex;
+      carry += total;
+    }
+    if (tid == 0) sh.pre[nsl] = carry;
     __syncthreads();
-    for (int s = tid; s < n; s += kThreads) atomicAdd(&sh.hist[order_key(sc[s]) >> 21], 1u);
+  }
+  const uint32_t M = sh.pre[nsl];
+  const bool in_lds = M <= (uint32_t)kCap;
+  const uint2* cand = a.cand + (int64_t)row * a.cand_ld;
+  // survivor e (in token order) -> (key, token index)
+  auto cand_at = [&](uint32_t e) -> uint2 {
+    int lo = 0, hi = nsl - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (sh.pre[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    return cand[lo * kTopkSlice + (int)(e - sh.pre[lo])];
+  };
+  if (in_lds) {
+    for (uint32_t e = tid; e < M; e += kResolveThreads) {
+      const uint2 kv = cand_at(e);
+      sh.key[e] = kv.x;
+      sh.idx[e] = (int32_t)kv.y;
+    }
+  }
+  auto key_of = [&](uint32_t e) -> uint32_t { return in_lds ? sh.key[e] : cand_at(e).x; };
+  auto tok_of = [&](uint32_t e) -> int32_t { return in_lds ? sh.idx[e] : (int32_t)cand_at(e).y; };
+
+  // level 1 from the histogram, which is then returned to zero for the next call
+  for (int i = tid; i < kBins; i += kResolveThreads) {
+    sh.hist[i] = hist_row[i];
+    hist_row[i] = 0;
   }
   __syncthreads();
   uint32_t need;
-  const uint32_t b1 = select_bin(sh, kBins, (uint32_t)k, &need);
+  const uint32_t b1 = select_bin<kResolveThreads>(sh.hist, kBins, (uint32_t)k, &need, sh.sc, sh.wtot);
 
-  // ---- compact the threshold bin's members into LDS
-  if (tid == 0) sh.bcast[3] = 0;
-  __syncthreads();
-  for (int s = tid; s < n; s += kThreads) {
-    const uint32_t key = order_key(sc[s]);
-    if ((key >> 21) == b1) {
-      const uint32_t p = atomicAdd(&sh.bcast[3], 1u);
-      if (p < kCap) {
-        sh.cand_key[p] = key;
-        sh.cand_idx[p] = s;
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t ncand = sh.bcast[3];
-  const bool in_lds = ncand <= (uint32_t)kCap;
-  __syncthreads();
-
-  // ---- levels 2 and 3: bits [20:10] and [9:0] among keys with the chosen prefix
+  // levels 2 and 3: key bits [20:10] and [9:0] among survivors sharing the chosen prefix
   uint32_t prefix = b1 << 21, mask = 0xFFE00000u;
-  const int shifts[2] = {10, 0};
-  const int widths[2] = {kBins, 1024};
+#pragma unroll
   for (int lev = 0; lev < 2; ++lev) {
-    const int sh_ = shifts[lev];
-    const uint32_t bmask = (uint32_t)widths[lev] - 1;
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0;
+    const int shift = lev == 0 ? 10 : 0;
+    const int nb = lev == 0 ? kBins : 1024;
+    const uint32_t bmask = (uint32_t)nb - 1;
+    for (int i = tid; i < kBins; i += kResolveThreads) sh.hist[i] = 0;
     __syncthreads();
-    if (in_lds) {
-      for (uint32_t c = tid; c < ncand; c += kThreads) {
-        const uint32_t key = sh.cand_key[c];
-        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> sh_) & bmask], 1u);
-      }
-    } else {
-      for (int s = tid; s < n; s += kThreads) {
-        const uint32_t key = order_key(sc[s]);
-        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> sh_) & bmask], 1u);
-      }
+    for (uint32_t e = tid; e < M; e += kResolveThreads) {
+      const uint32_t key = key_of(e);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & bmask], 1u);
     }
     __syncthreads();
-    uint32_t need2;
-    const uint32_t b = select_bin(sh, widths[lev], need, &need2);
-    need = need2;
-    prefix |= b << sh_;
-    mask |= bmask << sh_;
+    uint32_t rest;
+    const uint32_t b = select_bin<kResolveThreads>(sh.hist, nb, need, &rest, sh.sc, sh.wtot);
+    need = rest;
+    prefix |= b << shift;
+    mask |= bmask << shift;
   }
   const uint32_t T = prefix;  // exact key of the k-th largest score
-  const uint32_t E = need;    // keys equal to T that are selected (the lowest-index ones)
+  const uint32_t E = need;    // keys equal to T that make the cut (the lowest-index ones)
 
-  // ---- ordered selection pass
+  // ordered selection over the survivors (token order)
   uint32_t gt_run = 0, eq_run = 0;
-  const bool vec = ((a.ld & 3) == 0) && ((((uintptr_t)sc) & 15) == 0);
-  for (int base = 0; base < n; base += 4 * kThreads) {
-    const int s0 = base + 4 * tid;
+  for (uint32_t base = 0; base < M; base += 4 * kResolveThreads) {
+    const uint32_t e0 = base + 4 * tid;
     uint32_t key[4];
-    if (vec && s0 + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(sc + s0);
-      key[0] = order_key(v.x);
-      key[1] = order_key(v.y);
-      key[2] = order_key(v.z);
-      key[3] = order_key(v.w);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) key[j] = (s0 + j < n) ? order_key(sc[s0 + j]) : 0u;
-    }
+    for (int j = 0; j < 4; ++j) key[j] = (e0 + j < M) ? key_of(e0 + j) : 0u;
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool valid = s0 + j < n;
+      const bool valid = e0 + j < M;
       cgt += (valid && key[j] > T) ? 1u : 0u;
       ceq += (valid && key[j] == T) ? 1u : 0u;
     }
     uint32_t total;
-    const uint32_t ex = block_excl_scan(cgt | (ceq << 16), &total, sh);
+    const uint32_t ex = block_excl_scan<kResolveThreads>(cgt | (ceq << 16), &total, sh.wtot);
     uint32_t gt_before = gt_run + (ex & 0xFFFFu);
     uint32_t eq_before = eq_run + (ex >> 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s = s0 + j;
-      if (s >= n) break;
+      if (e0 + j >= M) break;
+      uint32_t slot = 0xFFFFFFFFu;
       if (key[j] > T) {
-        const uint32_t slot = gt_before + min(E, eq_before);
-        if (slot < (uint32_t)k) {
-          out[slot] = s;
-          if (phys) phys[slot] = phys_of(s);
-        }
+        slot = gt_before + min(E, eq_before);
         ++gt_before;
       } else if (key[j] == T) {
-        if (eq_before < E) {
-          const uint32_t slot = gt_before + eq_before;
-          if (slot < (uint32_t)k) {
-            out[slot] = s;
-            if (phys) phys[slot] = phys_of(s);
-          }
-        }
+        if (eq_before < E) slot = gt_before + eq_before;
         ++eq_before;
+      }
+      if (slot < (uint32_t)k) {
+        const int32_t s = tok_of(e0 + j);
+        out[slot] = s;
+        if (phys) phys[slot] = phys_of(s);
       }
     }
     gt_run += total & 0xFFFFu;
@@ -242,9 +312,36 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+size_t topk_workspace_bytes(int32_t num_rows, int64_t max_context) {
+  const int64_t ns = (max_context + kTopkSlice - 1) / kTopkSlice;
+  return (size_t)num_rows * (kBins + ns + 2 * ns * kTopkSlice + 2) * sizeof(uint32_t);
+}
+
+hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStream_t s) {
+  TopkArgs a = a0;
   if (a.batch.num_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.batch.num_rows), dim3(kThreads), 0, s, a);
+  const int64_t R = a.batch.num_rows;
+  a.num_slices = (int32_t)((max_context + kTopkSlice - 1) / kTopkSlice);
+  a.cand_ld = (int64_t)a.num_slices * kTopkSlice;
+  uint32_t* w = static_cast<uint32_t*>(ws);
+  uint32_t* hist_ws = w;
+  a.slice_cnt = w + R * kBins;
+  uint32_t* cand = a.slice_cnt + R * a.num_slices;
+  cand += ((uintptr_t)cand & 7) ? 1 : 0;  // 8-byte alignment of the (key, index) pairs
+  a.cand = reinterpret_cast<uint2*>(cand);
+  a.vec_ok = ((a.ld & 3) == 0) && ((((uintptr_t)a.scores) & 15) == 0);
+  hipError_t e;
+  if (a.hist_in == nullptr) {
+    if ((e = launch_zero_u32(hist_ws, R * kBins, s)) != hipSuccess) return e;
+    dim3 gh((unsigned)((max_context + kHistChunk - 1) / kHistChunk), (unsigned)R);
+    hipLaunchKernelGGL(topk_hist_kernel, gh, dim3(256), 0, s, a, hist_ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    a.hist_in = hist_ws;
+  }
+  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)a.num_slices, (unsigned)R),
+                     dim3(kFilterThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)R), dim3(kResolveThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -24,12 +24,17 @@ class DSALayer:
         decode_path = batch.c.max_rows_per_seq <= L.MAX_ROWS_PER_SEQ
         self.use_hist = decode_path if use_hist is None else (use_hist and decode_path)
         self.scores = torch.empty((R, self.ld), dtype=torch.float32, device=device)
-        self.hist = (torch.empty((R, L.HIST_BINS), dtype=torch.int32, device=device)
+        # zero on entry to the scorer; dsa_topk returns it to zero after consuming it
+        self.hist = (torch.zeros((R, L.HIST_BINS), dtype=torch.int32, device=device)
                      if self.use_hist else None)
         self.idx = torch.empty((R, k), dtype=torch.int32, device=device)
+        # pool rows of the selection, handed from the select to the attention
+        self.phys = torch.empty((R, k), dtype=torch.int32, device=device)
         self.count = torch.empty((R,), dtype=torch.int32, device=device)
         self.out = torch.empty((R, L.MLA_HEADS, L.MLA_DV), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((R, L.MLA_HEADS), dtype=torch.float32, device=device)
+        tb = L.dsa_topk_workspace_bytes(R, batch.c.max_context)
+        self.topk_ws = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=device)
         nbytes = 0 if prefill else L.sparse_mla_workspace_bytes(R, k)
         self.workspace = (torch.empty((max(nbytes, 16) + 15) // 16 * 4, dtype=torch.float32,
                                       device=device) if nbytes else None)
@@ -37,14 +42,16 @@ class DSALayer:
     def scores_step(self, pool, q_idx, w, stream=None):
         L.dsa_indexer_scores(self.kv, pool, self.batch, q_idx, w, self.scores, self.hist, stream)
 
-    def topk_step(self, stream=None, phys=None):
+    def topk_step(self, stream=None, phys=True):
         L.dsa_topk(self.kv, self.batch, self.scores, self.hist, self.k, self.idx, self.count,
-                   phys, stream)
+                   self.topk_ws, self.phys if phys else None, stream)
+        self.phys_valid = bool(phys)
 
-    def attention_step(self, pool, q, stream=None):
+    def attention_step(self, pool, q, stream=None, use_phys=None):
         fn = L.sparse_mla_prefill if self.prefill else L.sparse_mla_decode
+        use_phys = getattr(self, "phys_valid", False) if use_phys is None else use_phys
         fn(self.kv, pool, self.batch, q, self.idx, self.k, self.softmax_scale, self.out,
-           self.lse, self.workspace, stream)
+           self.lse, self.workspace, stream, phys=self.phys if use_phys else None)
 
     def run(self, pool, q_idx, w, q, stream=None):
         self.scores_step(pool, q_idx, w, stream)

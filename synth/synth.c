@@ -16,6 +16,7 @@
  * and FP8 keys take values k/4 with |k| <= 16, head weights k/4 with |k| <= wq, FP8 key scales
  * 2^-e with e in 0..6, and MXFP4 key block scales 2^-2..2^0.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -59,34 +60,51 @@ static inline double u01(uint64_t h) { /* (0,1), 53 bits */
   return ((double)(h >> 11) + 0.5) * (1.0 / 9007199254740992.0);
 }
 
-/* One standard normal per index (Box-Muller, cosine branch). */
+/* Two standard normals for element pair `pair` (elements 2*pair and 2*pair+1): Box-Muller on two
+ * 32-bit uniforms taken from one hash, in single precision. */
+static inline void normal_pair(uint64_t key, uint64_t pair, double* n0, double* n1) {
+  uint64_t h = mix64(key ^ (pair * 0xD1B54A32D192ED03ull));
+  float u1 = ((float)(uint32_t)(h >> 40) + 0.5f) * (1.0f / 16777216.0f);          /* (0,1) */
+  float u2 = (float)(uint32_t)(h & 0xFFFFFFu) * (1.0f / 16777216.0f);              /* [0,1) */
+  float r = sqrtf(-2.0f * logf(u1));
+  float sn, cs;
+  sincosf(6.2831853f * u2, &sn, &cs);
+  *n0 = (double)(r * cs);
+  *n1 = (double)(r * sn);
+}
+
+/* One standard normal per index (the matching half of its pair). */
 static inline double normal_at(uint64_t key, uint64_t index) {
-  uint64_t h1 = mix64(key ^ (index * 0xD1B54A32D192ED03ull));
-  uint64_t h2 = mix64(h1 ^ 0x5851F42D4C957F2Dull);
-  double u1 = u01(h1), u2 = u01(h2);
-  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2);
+  double a, b;
+  normal_pair(key, index >> 1, &a, &b);
+  return (index & 1) ? b : a;
 }
 
 /* ---------------------------------------------------------------- encoders (inputs only) */
 
-/* float -> OCP FP8 E4M3 code, round to nearest even, saturating to +-448. */
-uint8_t synth_enc_e4m3(double x) {
-  uint8_t s = (x < 0 || (x == 0 && signbit(x))) ? 0x80 : 0;
-  double a = fabs(x);
-  if (!(a == a)) return 0x7F; /* NaN in, NaN out (never generated) */
-  if (a >= 464.0) return s | 0x7E; /* saturate (464 is the midpoint 448..480) */
-  int e;
-  frexp(a, &e);          /* a = f * 2^e, f in [0.5,1) -> unbiased exponent e-1 */
-  int ue = e - 1;
-  if (a == 0) return s;
-  if (ue < -6) ue = -6;  /* subnormal range shares the 2^-6 binade's ulp */
-  double ulp = ldexp(1.0, ue - 3);
-  double r = nearbyint(a / ulp); /* default rounding mode = ties to even */
-  if (ue == -6 && r < 8) return s | (uint8_t)r; /* subnormal: value r * 2^-9 */
-  if (r >= 16) { r = 8; ue += 1; }
-  if (ue > 8 || (ue == 8 && r > 14)) return s | 0x7E;
-  return s | (uint8_t)(((ue + 7) << 3) | ((int)r - 8));
+/* float -> OCP FP8 E4M3 code, round to nearest even, saturating to +-448 (bit manipulation on
+ * the binary32 encoding: keep 3 mantissa bits with ties to even; below 2^-6 the step is 2^-9). */
+static inline uint8_t enc_e4m3_f(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  uint8_t s = (u >> 31) ? 0x80 : 0;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;  /* NaN (never generated) */
+  if (a >= 0x43E80000u) return s | 0x7E; /* |x| >= 464: saturate */
+  if (a < 0x3C800000u) {               /* |x| < 2^-6: subnormal grid m * 2^-9 */
+    float f;
+    memcpy(&f, &a, 4);
+    return s | (uint8_t)nearbyintf(f * 512.0f);  /* 8 rounds up to the smallest normal */
+  }
+  int e = (int)(a >> 23) - 127;
+  uint32_t m = a & 0x7FFFFFu;
+  uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20; /* 3 bits, ties to even */
+  if (r == 8) { r = 0; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | r;
+  return s | (uint8_t)(code > 0x7E ? 0x7E : code);
 }
+
+uint8_t synth_enc_e4m3(double x) { return enc_e4m3_f((float)x); }
 
 /* float -> OCP E2M1 nibble, round to nearest even, saturating to +-6. */
 uint8_t synth_enc_e2m1(double x) {
@@ -145,8 +163,12 @@ void synth_ikey_fp8(uint64_t seed, int64_t seq, int64_t tok0, int64_t ntok, uint
 #pragma omp parallel for schedule(static) if (ntok > 256)
   for (int64_t t = 0; t < ntok; ++t) {
     uint64_t s = (uint64_t)(tok0 + t);
-    for (int d = 0; d < IDX_DIM; ++d)
-      codes[t * IDX_DIM + d] = synth_enc_e4m3(grid_quarter(normal_at(kk, s * IDX_DIM + d), 16));
+    for (int d = 0; d < IDX_DIM; d += 2) {
+      double n0, n1;
+      normal_pair(kk, (s * IDX_DIM + d) >> 1, &n0, &n1);
+      codes[t * IDX_DIM + d] = synth_enc_e4m3(grid_quarter(n0, 16));
+      codes[t * IDX_DIM + d + 1] = synth_enc_e4m3(grid_quarter(n1, 16));
+    }
     int e = (int)(mix64(ks ^ (s * 0xD1B54A32D192ED03ull)) % 7u);
     scale[t] = (float)ldexp(1.0, -e);
   }
@@ -162,8 +184,10 @@ void synth_ikey_mxfp4(uint64_t seed, int64_t seq, int64_t tok0, int64_t ntok, ui
   for (int64_t t = 0; t < ntok; ++t) {
     uint64_t s = (uint64_t)(tok0 + t);
     for (int j = 0; j < IDX_DIM / 2; ++j) {
-      uint8_t lo = synth_enc_e2m1(2.0 * normal_at(kk, s * IDX_DIM + 2 * j));
-      uint8_t hi = synth_enc_e2m1(2.0 * normal_at(kk, s * IDX_DIM + 2 * j + 1));
+      double n0, n1;
+      normal_pair(kk, (s * IDX_DIM + 2 * j) >> 1, &n0, &n1);
+      uint8_t lo = synth_enc_e2m1(2.0 * n0);
+      uint8_t hi = synth_enc_e2m1(2.0 * n1);
       packed[t * 64 + j] = (uint8_t)(lo | (hi << 4));
     }
     for (int b = 0; b < 4; ++b)
@@ -179,8 +203,12 @@ void synth_latent_fp8(uint64_t seed, int64_t seq, int64_t tok0, int64_t ntok, ui
 #pragma omp parallel for schedule(static) if (ntok > 256)
   for (int64_t t = 0; t < ntok; ++t) {
     uint64_t s = (uint64_t)(tok0 + t);
-    for (int d = 0; d < MLA_DQK; ++d)
-      codes[t * MLA_DQK + d] = synth_enc_e4m3(normal_at(kk, s * MLA_DQK + d));
+    for (int d = 0; d < MLA_DQK; d += 2) {
+      double n0, n1;
+      normal_pair(kk, (s * MLA_DQK + d) >> 1, &n0, &n1);
+      codes[t * MLA_DQK + d] = synth_enc_e4m3(n0);
+      codes[t * MLA_DQK + d + 1] = synth_enc_e4m3(n1);
+    }
     scale[t] = (float)(0.5 + 1.5 * u01(mix64(ks ^ (s * 0xD1B54A32D192ED03ull))));
   }
 }
@@ -197,10 +225,9 @@ void synth_latent_nvfp4(uint64_t seed, int64_t seq, int64_t tok0, int64_t ntok, 
     double x[16];
     for (int b = 0; b < MLA_DQK / 16; ++b) {
       double amax = 0;
-      for (int i = 0; i < 16; ++i) {
-        x[i] = normal_at(kk, s * MLA_DQK + b * 16 + i);
+      for (int i = 0; i < 16; i += 2) normal_pair(kk, (s * MLA_DQK + b * 16 + i) >> 1, &x[i], &x[i + 1]);
+      for (int i = 0; i < 16; ++i)
         if (fabs(x[i]) > amax) amax = fabs(x[i]);
-      }
       double sv = round_to_e4m3_value(amax / 6.0);
       bscale[t * 36 + b] = synth_enc_e4m3(sv);
       for (int i = 0; i < 16; i += 2) {

@@ -13,7 +13,7 @@ import synth.device
 RTOL, ATOL = 2e-2, 2e-3  # bf16 outputs and fp32 log-sum-exp against the float64 oracle
 
 
-def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, phys=False):
+def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, phys=True):
     kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
     d = synth.device.stage(wl, kv.as_dict())
     if zero_qidx:
@@ -24,11 +24,13 @@ def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, ph
         prefill = d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ
     layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale, prefill=prefill, use_hist=use_hist)
     layer.scores_step(d["pool"], d["q_idx"], d["w"])
-    ph = torch.full((wl.num_rows, wl.k), -7, dtype=torch.int32, device="cuda") if phys else None
-    layer.topk_step(phys=ph)
+    if phys:
+        layer.phys.fill_(-7)
+    layer.topk_step(phys=phys)
     layer.attention_step(d["pool"], d["q"])
     torch.cuda.synchronize()
-    layer.phys = ph
+    if layer.hist is not None:  # dsa_topk returns the scorer's histogram to zero
+        assert int(layer.hist.abs().sum().item()) == 0
     return layer, d, kv
 
 

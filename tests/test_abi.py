@@ -89,20 +89,25 @@ def test_entry_points_validate_before_launch():
     # k out of range
     for k in (0, 2049):
         assert lib.dsa_topk(ctypes.byref(kv), ctypes.byref(b), p, 128, None, k, p, p, None,
-                            None) == L.DSA_ERR_INVALID_ARG
-        assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b), p, p, k, 0.1, p,
-                                     None, None, 0, None) == L.DSA_ERR_INVALID_ARG
+                            p, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
+        assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b), p, p, None, k, 0.1,
+                                     p, None, None, 0, None) == L.DSA_ERR_INVALID_ARG
     # phys rows need the layout
-    assert lib.dsa_topk(None, ctypes.byref(b), p, 128, None, 16, p, p, p, None) == \
+    assert lib.dsa_topk(None, ctypes.byref(b), p, 128, None, 16, p, p, p, p, 1 << 30, None) == \
         L.DSA_ERR_INVALID_ARG
+    # top-k needs its workspace
+    need = lib.dsa_topk_workspace_bytes(1, 100)
+    assert need > 0
+    assert lib.dsa_topk(ctypes.byref(kv), ctypes.byref(b), p, 128, None, 16, p, p, None, p,
+                        need - 1, None) == L.DSA_ERR_WORKSPACE
     # decode MLA with several splits needs its workspace
     b3 = _fake_batch(num_rows=1)
     need = lib.sparse_mla_workspace_bytes(1, 2048)
     assert need > 0
-    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, 2048, 0.1, p,
-                                 None, None, 0, None) == L.DSA_ERR_WORKSPACE
-    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, 2048, 0.1, p,
-                                 None, p, need - 1, None) == L.DSA_ERR_WORKSPACE
+    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, None, 2048, 0.1,
+                                 p, None, None, 0, None) == L.DSA_ERR_WORKSPACE
+    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, p, 2048, 0.1,
+                                 p, None, p, need - 1, None) == L.DSA_ERR_WORKSPACE
     # MXFP4 keys on the prefill path are not built
     kv4 = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_FP8, 10)
     b4 = _fake_batch(max_rows_per_seq=64, num_rows=64)
