@@ -105,7 +105,9 @@ typedef struct dsa_kv_layout {
 typedef struct dsa_batch {
   int32_t num_seqs;
   int32_t num_rows;
-  int32_t max_rows_per_seq;   /* host: upper bound on rows of any one sequence */
+  int32_t max_rows_per_seq;   /* host: upper bound on rows of any one sequence (>= 1; 0 only
+                                 when num_rows is 0: every entry point then returns DSA_OK
+                                 and launches nothing) */
   int32_t max_blocks_per_seq; /* host: leading dimension of block_table */
   int64_t max_context;        /* host: upper bound on row_pos[r] + 1 over all rows */
   const int32_t* block_table;   /* [num_seqs * max_blocks_per_seq] pool row ids */

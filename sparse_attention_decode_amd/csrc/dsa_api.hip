@@ -55,7 +55,8 @@ dsa_status check_batch(const dsa_batch* b) {
   if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
   if (b->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "num_seqs must be >= 1");
   if (b->num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "num_rows must be >= 0");
-  if (b->max_rows_per_seq < 1) return fail(DSA_ERR_INVALID_ARG, "max_rows_per_seq must be >= 1");
+  if (b->max_rows_per_seq < (b->num_rows > 0 ? 1 : 0))
+    return fail(DSA_ERR_INVALID_ARG, "max_rows_per_seq must be >= 1 when num_rows > 0");
   if (b->max_context < 1) return fail(DSA_ERR_INVALID_ARG, "max_context must be >= 1");
   if (b->max_context > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "max_context too large");
   if ((int64_t)b->max_blocks_per_seq * 64 < b->max_context)

@@ -114,3 +114,21 @@ def test_entry_points_validate_before_launch():
     assert lib.dsa_indexer_scores(ctypes.byref(kv4), pool, ctypes.byref(b4), p, p, p, 128, None,
                                   None) == L.DSA_ERR_UNSUPPORTED
     assert lib.dsa_status_string(L.DSA_ERR_WORKSPACE) == b"DSA_ERR_WORKSPACE"
+
+
+def test_empty_batch_is_a_no_op():
+    # A batch with no query rows validates and returns DSA_OK without launching anything.
+    lib = L.lib()
+    kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    pool = ctypes.c_void_p(0x100000)
+    p = ctypes.c_void_p(0x2000)
+    b = _fake_batch(num_rows=0, max_rows_per_seq=0)
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), pool, ctypes.byref(b), p, p, p, 128, p,
+                                  None) == L.DSA_OK
+    assert lib.dsa_topk_workspace_bytes(0, 100) == 0
+    assert lib.dsa_topk(ctypes.byref(kv), ctypes.byref(b), p, 128, p, 16, p, p, p, None, 0,
+                        None) == L.DSA_OK
+    assert lib.sparse_mla_workspace_bytes(0, 2048) == 0
+    for fn in (lib.sparse_mla_decode, lib.sparse_mla_prefill):
+        assert fn(ctypes.byref(kv), pool, ctypes.byref(b), p, p, p, 2048, 0.1, p, None, None, 0,
+                  None) == L.DSA_OK
