@@ -17,8 +17,11 @@
 // (288 of the 576 dims) and the half d of the output dims (256 of 512), so a wave holds 36 query
 // registers and 64 accumulator registers, and three waves share each SIMD.  Tiles of 32 selected
 // tokens are gathered from the paged pool straight into LDS with direct global->LDS loads (no
-// registers held in flight), three stages deep so the gathers of tiles j+1 and j+2 overlap the
-// math of tile j.
+// registers held in flight), kStages - 1 tiles ahead of the tile being processed.  Each stage is
+// its own LDS variable and barriers wait on LDS traffic only, so reading a tile never waits for
+// the gathers of later tiles.  The pool rows to gather are handed over in a lane-distributed
+// register (one batch of 21 tiles per register), read with readlane: no memory round trip sits
+// between a tile and its gathers.
 //   QK^T: S^T[tokens x heads] = C Q^T on bf16 MFMA.  The query stays in registers (B operand);
 //         the latent tile is the A operand.  FP8 latents are read raw from LDS and converted to
 //         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
@@ -46,9 +49,17 @@ constexpr int kThreadsM = kWavesM * kWave;        // 768
 constexpr int kTile = 32;                         // selected tokens per tile
 constexpr int kSteps = DSA_MLA_DQK / 32 / 2;      // 9 K steps of 32 dims per wave (half of 576)
 constexpr int kDvHalf = DSA_MLA_DV / 2;           // 256 output dims per wave
-constexpr int kPhysRing = 512;                // pool rows of upcoming selected tokens
-constexpr int kStages = 3;                    // gather pipeline: tiles j, j+1, j+2 in flight
+#ifndef DSA_MLA_STAGES
+#define DSA_MLA_STAGES 4
+#endif
+// Gather pipeline: while tile j is processed, tiles j+1 .. j+kAhead are in flight.
+constexpr int kStages = DSA_MLA_STAGES;
+constexpr int kAhead = kStages - 1;
+static_assert(kStages >= 3 && kStages <= 6, "stage variables raw0..raw5");
 constexpr int kRowsPerWave = (kTile + kWavesM - 1) / kWavesM;  // 3 (rows >= 32 are dummies)
+// Pool rows of a wave's gathers, one register per batch of tiles: lane 3T + r holds the row of
+// tile T's row r of the batch (kBatchTiles tiles per register).
+constexpr int kBatchTiles = kWave / kRowsPerWave;  // 21
 // Every wave issues exactly this many gathers per tile (data + scale per row, dummies included),
 // so waiting for a tile is "all but the newest tile's gathers are done".
 constexpr int kGathersPerWave = 2 * kRowsPerWave;
@@ -95,23 +106,29 @@ __device__ __forceinline__ int vt_pos(int t) {
 }
 
 // Issue the direct global->LDS gathers of tile j (selected slots [j, min(j+32, jend))) into stage
-// st.  Wave w gathers tile rows w, w+12, w+24; rows past the tile and slots without a token
-// gather a harmless dummy (pool row 0) into `junk`, so that every wave issues kGathersPerWave
-// loads per tile.
+// st.  Wave w gathers tile rows w, w+12, w+24, whose pool rows are lanes lb, lb+1, lb+2 of `pv`.
+// Rows past the tile and slots without a token gather a dummy into `junk`, so that every wave
+// issues kGathersPerWave loads per tile: the wave's first real row of the tile again if it has
+// one, else a pool row that depends on the workgroup and wave (never one row for everybody:
+// thousands of requests to one address would queue on one memory channel).
 template <int LFMT>
-__device__ __forceinline__ void issue_tile(const Stage& st, const int32_t* phys, uint8_t* junk,
-                                           const MlaArgs& a, int j, int jend, int j0) {
+__device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, uint8_t* junk,
+                                           const MlaArgs& a, int j, int jend) {
   using G = Geo<LFMT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ph_first = (j + wave < jend) ? __builtin_amdgcn_readlane(pv, lb) : -1;
+  const int ph_spread =
+      (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens);
+  const int ph_dummy = ph_first >= 0 ? ph_first : ph_spread;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int t = wave + kWavesM * r;
     const int jj = j + t;
-    const int ph = __builtin_amdgcn_readfirstlane(
-        (t < kTile && jj < jend) ? phys[(jj - j0) % kPhysRing] : -1);  // wave-uniform
+    const int ph = (t < kTile && jj < jend) ? __builtin_amdgcn_readlane(pv, lb + r) : -1;
     if (t < kTile && lane == 0) st.valid[t] = ph >= 0;
-    const uint8_t* row = a.pool.base + (int64_t)(ph >= 0 ? ph / kBlock : 0) * a.pool.row_bytes;
-    const int slot = ph >= 0 ? ph % kBlock : 0;
+    const int src = ph >= 0 ? ph : ph_dummy;
+    const uint8_t* row = a.pool.base + (int64_t)(src / kBlock) * a.pool.row_bytes;
+    const int slot = src % kBlock;
     uint8_t* dst = t < kTile ? st.raw + t * G::kRaw : junk;
     if constexpr (G::kFp8) {
       float* dsc = t < kTile ? st.tsc + t : reinterpret_cast<float*>(junk + kRaw8);
@@ -238,19 +255,21 @@ __device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int g) {
 template <int LFMT>
 __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   using G = Geo<LFMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t raw0[kTile * G::kRaw];
-  __shared__ __attribute__((aligned(16))) uint8_t raw1[kTile * G::kRaw];
-  __shared__ __attribute__((aligned(16))) uint8_t raw2[kTile * G::kRaw];
-  __shared__ float tsc0[kTile], tsc1[kTile], tsc2[kTile];
-  __shared__ int32_t valid0[kTile], valid1[kTile], valid2[kTile];
+  constexpr int kRawBytes = kTile * G::kRaw;
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[kRawBytes], raw1[kRawBytes], raw2[kRawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t raw3[kStages > 3 ? kRawBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t raw4[kStages > 4 ? kRawBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t raw5[kStages > 5 ? kRawBytes : 16];
+  __shared__ float tsc0[kTile], tsc1[kTile], tsc2[kTile], tsc3[kTile], tsc4[kTile], tsc5[kTile];
+  __shared__ int32_t valid0[kTile], valid1[kTile], valid2[kTile], valid3[kTile], valid4[kTile],
+      valid5[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
   __shared__ __attribute__((aligned(16))) v4f sx[kWavesM][2][kWave];  // partial S^T exchange
   __shared__ float amx[kWavesM][16];
-  __shared__ int32_t phys[kPhysRing];
   __shared__ __attribute__((aligned(16))) uint8_t junk[G::kRaw + 16];  // dummy gathers land here
-  static_assert(kStages == 3, "three stage variables");
-  const Stage stages[kStages] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2}};
+  const Stage stages[6] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2},
+                           {raw3, tsc3, valid3}, {raw4, tsc4, valid4}, {raw5, tsc5, valid5}};
 
   const int row = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -275,11 +294,15 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   }
 
-  // Pool rows of the selected tokens, kept kPhysRing/2 .. kPhysRing slots ahead of the tile being
-  // gathered: [j0, j0 + kPhysRing) now, then every kPhysRing/2 slots the next half.
-  auto fill_phys = [&](int from, int to) {
-    for (int jj = from + tid; jj < min(to, j1); jj += kThreadsM) {
-      int ph;
+  // Pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane 3T + r:
+  // tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  auto load_batch = [&](int tb) {
+    const int T = lane / kRowsPerWave, r = lane % kRowsPerWave;
+    const int t = wave + kWavesM * r;
+    const int jj = j0 + kTile * (tb + T) + t;
+    int ph = -1;
+    if (T < kBatchTiles && t < kTile && jj < j1) {
       if (prow) {
         ph = prow[jj];
         if (ph >= a.pool.tokens) ph = -1;
@@ -287,10 +310,15 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         const int s = idx[jj];
         ph = (s >= 0 && s < nvis) ? bt[s / kBlock] * kBlock + (s % kBlock) : -1;
       }
-      phys[(jj - j0) % kPhysRing] = ph;
     }
+    return ph;
   };
 
+  // Prologue: the pool rows of the first batches are loaded first (the gathers wait for them);
+  // the query loads are issued right behind them and complete under the first gathers.
+  int tb = 0;
+  int pv = load_batch(0);
+  int pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : -1;
   // Q^T fragments (B operand) of this wave's half of the contraction
   const int kd = kHalfDims * dh;  // first dim of the half (wave-uniform)
   v8bf qf[kSteps];
@@ -300,14 +328,15 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     for (int i = 0; i < kSteps; ++i)
       qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 32 * i));
   }
-  fill_phys(j0, j0 + kPhysRing);
-  // Consume the query registers before any gather is issued: the compiler's wait for them is then
-  // a wait for loads that are done anyway, not a full wait inside the loop.
+  if (ntiles > 0) issue_tile<LFMT>(stages[0], pv, 0, junk, a, j0, j1);
+  // Consume the query registers between the first two tiles' gathers: the compiler cannot count
+  // the gathers (they sit behind lane conditions), so its wait for the query is a full wait; here
+  // that covers the query and tile 0 only, and keeps it out of the loop.
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) asm volatile("" ::"v"(qf[i]));
-  lds_barrier();
-  issue_tile<LFMT>(stages[0], phys, junk, a, j0, j1, j0);
-  issue_tile<LFMT>(stages[1], phys, junk, a, j0 + kTile, j1, j0);
+#pragma unroll
+  for (int T = 1; T < kAhead; ++T)
+    if (T < ntiles) issue_tile<LFMT>(stages[T], pv, kRowsPerWave * T, junk, a, j0 + T * kTile, j1);
 
   v4f o[kDvHalf / 16];
 #pragma unroll
@@ -321,16 +350,22 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       const int j = jb + s * kTile;
       if (j >= j1) break;
       const Stage& cur = stages[s];
-      // all but the newest tile's gathers are done: tile j has landed (this wave's part)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGathersPerWave) : "memory");
+      // All but the gathers of the tiles issued after tile j are done: tile j has landed (this
+      // wave's part).  Tiles past the split's end are never issued, so near the end fewer are.
+      {
+        const int newer = min(kAhead - 1, ntiles - 1 - (j - j0) / kTile);
+        static_assert(kAhead - 1 <= 4, "wait counts below");
+        if (newer >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kGathersPerWave) : "memory");
+        else if (newer == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kGathersPerWave) : "memory");
+        else if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGathersPerWave) : "memory");
+        else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGathersPerWave) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
-      if ((j - j0) % (kPhysRing / 2) == 0 && j > j0)
-        fill_phys(j + kPhysRing / 2, j + kPhysRing);  // overwrites slots already gathered
       if constexpr (G::kFp8)
         build_fp8(cur, vt);
       else
         build_nvfp4(cur, ct, vt);
-      issue_tile<LFMT>(stages[(s + 2) % kStages], phys, junk, a, j + 2 * kTile, j1, j0);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
       // this wave's half of S^T (tokens x heads) for the two 16-token halves of the tile
@@ -401,6 +436,21 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
       for (int mt = 0; mt < kDvHalf / 16; ++mt)
         o[mt] = mfma_f16(pv_operand<LFMT>(vt, kDvHalf * dh + 16 * mt + c, g), pfrag, o[mt]);
+
+      // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
+      // first barrier, so no one reads it any more).  Issued last: a wave that finds the gather
+      // queue full stalls here, where it would otherwise wait at the next barrier.
+      {
+        const int T = (j - j0) / kTile + kAhead;
+        if (T - tb == kBatchTiles) {  // next batch of pool rows (loaded one batch ahead)
+          tb += kBatchTiles;
+          pv = pv_next;
+          if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
+        }
+        if (T < ntiles)
+          issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, kRowsPerWave * (T - tb), junk, a,
+                           j + kAhead * kTile, j1);
+      }
     }
   }
 
@@ -427,13 +477,16 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   } else {
     // Split partial: this split's normalised output as fp16 scaled by a power of two chosen from
     // the head's largest value in the split (11 significant bits relative to that value, for any
-    // latent scale), the scale's exponent, and the split's base-2 log-sum-exp.
+    // latent scale), the scale's exponent, and the split's base-2 log-sum-exp.  The fp16 values
+    // keep the accumulator layout (wave, mt, lane, 4 values), so every store is 512 contiguous
+    // bytes.
     const int64_t slot = ((int64_t)row * a.nsplit + split) * DSA_MLA_HEADS + head;
     float amax = 0.f;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[mt][i] * inv));
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[mt][0]), fabsf(o[mt][1])),
+                               fmaxf(fabsf(o[mt][2]), fabsf(o[mt][3]))));
+    amax *= inv;
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
     if (g == 0) amx[wave][c] = amax;
@@ -442,12 +495,12 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     // 2^e * amax lies in [2^14, 2^15): well inside fp16's range and above its subnormals
     const int e = (amax > 0.f) ? 14 - ilogbf(amax) : 0;
     const float sc = inv * ldexpf(1.f, e);
-    uint16_t* po = a.part_o + slot * DSA_MLA_DV + kDvHalf * dh;
+    uint2* po = reinterpret_cast<uint2*>(a.part_o) +
+                (((int64_t)row * a.nsplit + split) * kWavesM + wave) * (kDvHalf / 16) * kWave + lane;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt)
-      *reinterpret_cast<uint2*>(po + 16 * mt + 4 * g) =
-          uint2{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
-                f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
+      po[mt * kWave] = uint2{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
+                             f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
     if (g == 0 && dh == 0) {
       a.part_lse[slot] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
       a.part_exp[slot] = e;
@@ -456,13 +509,22 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 }
 
 // Merge the splits of each row by log-sum-exp: out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
-// with o_s the split's normalised output.  grid (rows, 96 heads / 2); 256 threads: two heads,
-// 128 threads x 4 dims each.
-__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
+// with o_s the split's normalised output.  grid (rows, 12 waves x 2 halves); 512 threads: thread
+// (mt8, lane) takes accumulator block mt = 8 * blockIdx.y % 2 + mt8 of the attention wave
+// blockIdx.y / 2, i.e. head 16 * (wave / 2) + lane % 16, dims 256 * (wave % 2) + 16 mt + 4 (lane / 16)
+// + 0..3.  Partial loads are 8 contiguous bytes per thread (4 KB per workgroup and split).
+__global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   const int row = blockIdx.x;
-  const int head = 2 * blockIdx.y + (threadIdx.x >> 7);
-  const int d = 4 * (threadIdx.x & 127);
-  const int64_t base = (int64_t)row * a.nsplit * DSA_MLA_HEADS + head;
+  const int wave = blockIdx.y >> 1;
+  const int mt = 8 * (blockIdx.y & 1) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int head = 16 * (wave >> 1) + (lane & 15);
+  const int d = kDvHalf * (wave & 1) + 16 * mt + 4 * (lane >> 4);
+  const int64_t hbase = (int64_t)row * a.nsplit * DSA_MLA_HEADS + head;
+  const uint2* pbase = reinterpret_cast<const uint2*>(a.part_o) +
+                       ((int64_t)row * a.nsplit * kWavesM + wave) * (kDvHalf / 16) * kWave +
+                       mt * kWave + lane;
+  const int64_t pstride = (int64_t)kWavesM * (kDvHalf / 16) * kWave;  // one split
   // splits in groups of 8 with every load of a group issued before it is used
   constexpr int G = 8;
   float M = -INFINITY;
@@ -470,7 +532,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
     float ls[G];
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      ls[u] = s0 + u < a.nsplit ? a.part_lse[base + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
+      ls[u] = s0 + u < a.nsplit ? a.part_lse[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
 #pragma unroll
     for (int u = 0; u < G; ++u) M = fmaxf(M, ls[u]);
   }
@@ -483,16 +545,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
       uint2 v[G];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
-        const int64_t slot = base + (int64_t)(s0 + u) * DSA_MLA_HEADS;
         const bool in = s0 + u < a.nsplit;
-        ls[u] = in ? a.part_lse[slot] : -INFINITY;
-        ex[u] = in ? a.part_exp[slot] : 0;
-        v[u] = in ? *reinterpret_cast<const uint2*>(a.part_o + slot * DSA_MLA_DV + d) : uint2{0u, 0u};
+        ls[u] = in ? a.part_lse[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
+        ex[u] = in ? a.part_exp[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : 0;
+        v[u] = in ? pbase[(int64_t)(s0 + u) * pstride] : uint2{0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
-        if (ls[u] == -INFINITY) continue;
-        const float wgt = exp2f(ls[u] - M);
+        const float wgt = (ls[u] == -INFINITY) ? 0.f : exp2f(ls[u] - M);
         L += wgt;
         const float w2 = ldexpf(wgt, -ex[u]);
         acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
@@ -511,7 +571,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   }
   *reinterpret_cast<uint2*>(a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + d) =
       uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-  if (a.lse && d == 0)
+  if (a.lse && mt == 0 && (wave & 1) == 0 && lane < 16)
     a.lse[(int64_t)row * DSA_MLA_HEADS + head] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -543,8 +603,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
     hipLaunchKernelGGL(sparse_mla_kernel<DSA_LATENT_NVFP4>, grid, dim3(kThreadsM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)a.batch.num_rows, DSA_MLA_HEADS / 2),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)a.batch.num_rows, 2 * kWavesM),
+                     dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
