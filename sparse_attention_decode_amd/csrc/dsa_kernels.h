@@ -24,6 +24,7 @@ struct IndexerArgs {
   int64_t ld;
   uint32_t* hist;    // [R][2048] or null
   int32_t tiles_per_seq;  // row tiles per sequence (1 on the decode path)
+  int32_t pages_per_wave; // multi-row scorer: key pages per wave (a multiple of 4)
 };
 
 // Decode / speculative decode scorer: grid (chunks, num_seqs).

@@ -194,9 +194,159 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
   }
 }
 
+// Several rows per sequence (speculative verification: 3..8 rows).  Same scoring as above, with
+// the rows' queries and head weights in LDS instead of registers (registers for 6-8 rows would
+// leave one wave per SIMD), and each workgroup walking a long run of pages in groups of four
+// (fewer workgroups, so fewer histogram flushes).  Scores leave after each group of four pages.
+template <int R, int KFMT, bool HIST>
+__global__ __launch_bounds__(kThreads) void indexer_rows_kernel(IndexerArgs a) {
+  constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
+  __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
+  __shared__ uint32_t s_hist[HIST ? R * kBins : 1];
+  const int seq = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+
+  const int r0 = a.batch.seq_row_start[seq];
+  const int nr = min(R, a.batch.seq_row_start[seq + 1] - r0);
+  if (nr <= 0) return;
+  int pos[R];
+  int L = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pos[r] = r < nr ? a.batch.row_pos[r0 + r] : -1;
+    L = max(L, pos[r] + 1);
+  }
+  const int nblk = (L + kBlock - 1) / kBlock;
+  constexpr int kWaves = kThreads / kWave;
+  const int ppw = a.pages_per_wave;
+  const int blk0 = blockIdx.x * kWaves * ppw;
+  if (blk0 >= nblk) return;
+
+  // queries (rows past nr repeat the last row; their results are never used) and weights
+  for (int i = tid; i < R * DSA_INDEX_HEADS * (DSA_INDEX_DIM / 16); i += kThreads) {
+    const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
+    const int r = rh / DSA_INDEX_HEADS, h = rh % DSA_INDEX_HEADS;
+    const int row = r0 + min(r, nr - 1);
+    *reinterpret_cast<uint4*>(&s_q[rh * kQRow + 16 * ch]) =
+        *reinterpret_cast<const uint4*>(a.q + ((int64_t)row * DSA_INDEX_HEADS + h) * DSA_INDEX_DIM + 16 * ch);
+  }
+  for (int i = tid; i < R * DSA_INDEX_HEADS; i += kThreads) {
+    const int r = i / DSA_INDEX_HEADS;
+    s_w[i] = a.w[(int64_t)(r0 + min(r, nr - 1)) * DSA_INDEX_HEADS + i % DSA_INDEX_HEADS];
+  }
+  if (HIST)
+    for (int i = tid; i < R * kBins; i += kThreads) s_hist[i] = 0;
+  __syncthreads();
+
+  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
+  auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
+  auto load_page = [&](KeyFrag* f, int i) {
+    const int blk = page_of(i);
+    if (i < ppw && blk < nblk) {
+      const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
+    }
+  };
+  KeyFrag buf[2][4];
+  load_page(buf[0], 0);
+  for (int i0 = 0; i0 < ppw; i0 += 4) {
+    if (page_of(i0) >= nblk) break;
+    float sbuf[R][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u;
+      load_page(buf[(u + 1) & 1], i + 1);
+      if (i >= ppw || page_of(i) >= nblk) break;
+      const KeyFrag* cur = buf[u & 1];
+      const int blk = page_of(i);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r >= nr) break;
+        v8i qa[2];
+        float wv[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const uint8_t* qr = &s_q[(r * DSA_INDEX_HEADS + 16 * mt + c) * kQRow];
+          const uint4 lo = *reinterpret_cast<const uint4*>(qr + 16 * g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(qr + 64 + 16 * g);
+          qa[mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                       (int)hi.w};
+          const float4 w4 = *reinterpret_cast<const float4*>(&s_w[r * DSA_INDEX_HEADS + 16 * mt + 4 * g]);
+          wv[mt][0] = w4.x; wv[mt][1] = w4.y; wv[mt][2] = w4.z; wv[mt][3] = w4.w;
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          v4f z = {0.f, 0.f, 0.f, 0.f};
+          v4f acc0, acc1;
+          if (KFMT == DSA_IKEY_FP8) {
+            acc0 = mfma_fp8(qa[0], cur[nt].b, z);
+            acc1 = mfma_fp8(qa[1], cur[nt].b, z);
+          } else {
+            acc0 = mfma_fp8_fp4(qa[0], cur[nt].b, z, 127, cur[nt].escale);
+            acc1 = mfma_fp8_fp4(qa[1], cur[nt].b, z, 127, cur[nt].escale);
+          }
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part += wv[0][e] * fmaxf(acc0[e], 0.f);
+            part += wv[1][e] * fmaxf(acc1[e], 0.f);
+          }
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+          if (g == nt) mine = part * cur[nt].scale;
+        }
+        sbuf[r][u] = mine;
+        if (HIST && blk * kBlock + lane <= pos[r])
+          atomicAdd(&s_hist[r * kBins + (order_key(mine) >> 21)], 1u);
+      }
+    }
+    // one coalesced 256-byte store per (page, row) of the group
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u;
+      if (i >= ppw || page_of(i) >= nblk) break;
+      const int s = page_of(i) * kBlock + lane;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < nr && s <= pos[r]) a.scores[(int64_t)(r0 + r) * a.ld + s] = sbuf[r][u];
+    }
+  }
+
+  if (HIST) {
+    __syncthreads();
+    for (int i = tid; i < nr * kBins; i += kThreads) {
+      const uint32_t v = s_hist[i];
+      if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
+    }
+  }
+}
+
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+template <int KFMT>
+hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s) {
+  switch (rows) {
+#define DSA_CASE(R)                                                                            \
+  case R:                                                                                      \
+    if (a.hist)                                                                                \
+      hipLaunchKernelGGL((indexer_rows_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
+    else                                                                                       \
+      hipLaunchKernelGGL((indexer_rows_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
+    break;
+    DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
+#undef DSA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int KFMT>
@@ -233,6 +383,20 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   IndexerArgs a = a0;
   a.tiles_per_seq = 1;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
+  if (rows_per_seq >= 3) {
+    // about 2048 workgroups in all: pages per wave a multiple of 4 in [4, 64]
+    constexpr int kWaves = kThreads / kWave;
+    const int64_t want = (nblk * a.batch.num_seqs + 2047) / 2048;
+    int64_t ppw = (want + kWaves - 1) / kWaves;
+    ppw = (ppw + 3) / 4 * 4;
+    if (ppw < 4) ppw = 4;
+    if (ppw > 64) ppw = 64;
+    a.pages_per_wave = (int32_t)ppw;
+    const int64_t per_wg = ppw * kWaves;
+    dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg), (unsigned)a.batch.num_seqs);
+    return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
+                                    : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
+  }
   dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)a.batch.num_seqs);
   return ikey_fmt == DSA_IKEY_FP8 ? launch_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
                                   : launch_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
