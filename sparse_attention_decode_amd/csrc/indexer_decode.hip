@@ -31,6 +31,7 @@ constexpr int kThreads = 256;         // 4 waves
 constexpr int kBlocksPerWave = DSA_IDX_PAGES_PER_WAVE;  // 64-token pages per wave per workgroup
 constexpr int kBlocksPerWG = kBlocksPerWave * (kThreads / kWave);
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
+constexpr int kPrefillRows = 16;      // rows per workgroup tile on the prefill path
 
 // Operand fragments of one 16-token tile.
 struct KeyFrag {
@@ -120,7 +121,9 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
   auto load_page = [&](KeyFrag* f, int i) {
     const int blk = page_of(i);
     if (i < kBlocksPerWave && blk < nblk) {
-      const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
+      // the page's pool row is wave-uniform: scalar base, 32-bit lane offsets
+      const uint8_t* row =
+          a.pool.base + (int64_t)__builtin_amdgcn_readfirstlane(bt[blk]) * a.pool.row_bytes;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
     }
@@ -165,8 +168,7 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
             part += wv[r][0][e] * fmaxf(acc0[e], 0.f);
             part += wv[r][1][e] * fmaxf(acc1[e], 0.f);
           }
-          part += __shfl_xor(part, 16, 64);
-          part += __shfl_xor(part, 32, 64);
+          part = xor32_sum(xor16_sum(part));
           if (g == nt) mine = part * cur[nt].scale;
         }
         sbuf[r][i] = mine;
@@ -194,23 +196,28 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
   }
 }
 
-// Several rows per sequence (speculative verification: 3..8 rows).  Same scoring as above, with
-// the rows' queries and head weights in LDS instead of registers (registers for 6-8 rows would
-// leave one wave per SIMD), and each workgroup walking a long run of pages in groups of four
-// (fewer workgroups, so fewer histogram flushes).  Scores leave after each group of four pages.
+// Several rows per sequence: speculative verification (3..8 rows of one sequence) and prefill
+// (tiles of 16 rows of a chunk).  Same scoring as above, with the rows' queries and head weights
+// in LDS instead of registers (registers for 6-16 rows would leave one wave per SIMD), and each
+// workgroup walking a long run of pages in groups of G (fewer workgroups, so fewer histogram
+// flushes, and every key byte read once per row tile).  Scores leave after each group.
 template <int R, int KFMT, bool HIST>
-__global__ __launch_bounds__(kThreads) void indexer_rows_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void indexer_rows_kernel(IndexerArgs a) {
+  constexpr int G = R <= 8 ? 4 : 2;  // pages per store group
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? R * kBins : 1];
-  const int seq = blockIdx.y;
+  // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
+  const int seq = blockIdx.y / a.tiles_per_seq;
+  const int tile = blockIdx.y % a.tiles_per_seq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
 
-  const int r0 = a.batch.seq_row_start[seq];
-  const int nr = min(R, a.batch.seq_row_start[seq + 1] - r0);
+  const int r0 = __builtin_amdgcn_readfirstlane(a.batch.seq_row_start[seq] + tile * R);
+  const int nr = __builtin_amdgcn_readfirstlane(min(R, a.batch.seq_row_start[seq + 1] - r0));
   if (nr <= 0) return;
   int pos[R];
   int L = 0;
@@ -246,26 +253,31 @@ __global__ __launch_bounds__(kThreads) void indexer_rows_kernel(IndexerArgs a) {
   auto load_page = [&](KeyFrag* f, int i) {
     const int blk = page_of(i);
     if (i < ppw && blk < nblk) {
-      const uint8_t* row = a.pool.base + (int64_t)bt[blk] * a.pool.row_bytes;
+      // the page's pool row is wave-uniform: scalar base, 32-bit lane offsets
+      const uint8_t* row =
+          a.pool.base + (int64_t)__builtin_amdgcn_readfirstlane(bt[blk]) * a.pool.row_bytes;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
     }
   };
   KeyFrag buf[2][4];
   load_page(buf[0], 0);
-  for (int i0 = 0; i0 < ppw; i0 += 4) {
+#pragma unroll 1
+  for (int i0 = 0; i0 < ppw; i0 += G) {
     if (page_of(i0) >= nblk) break;
-    float sbuf[R][4];
+    float sbuf[R][G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
       load_page(buf[(u + 1) & 1], i + 1);
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const int blk = page_of(i);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (r >= nr) break;
+      for (int r = 0; r < R; ++r) {  // all R rows (rows past nr score with the last row's query)
+        // Reload the row's query and weights from LDS here: hoisted out of the page loop they
+        // would hold 24 registers per row for the whole kernel.
+        asm volatile("" ::: "memory");
         v8i qa[2];
         float wv[2][4];
 #pragma unroll
@@ -296,24 +308,28 @@ __global__ __launch_bounds__(kThreads) void indexer_rows_kernel(IndexerArgs a) {
             part += wv[0][e] * fmaxf(acc0[e], 0.f);
             part += wv[1][e] * fmaxf(acc1[e], 0.f);
           }
-          part += __shfl_xor(part, 16, 64);
-          part += __shfl_xor(part, 32, 64);
+          part = xor32_sum(xor16_sum(part));
           if (g == nt) mine = part * cur[nt].scale;
         }
         sbuf[r][u] = mine;
-        if (HIST && blk * kBlock + lane <= pos[r])
+        if (HIST && r < nr && blk * kBlock + lane <= pos[r])
           atomicAdd(&s_hist[r * kBins + (order_key(mine) >> 21)], 1u);
       }
     }
     // one coalesced 256-byte store per (page, row) of the group
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
       if (i >= ppw || page_of(i) >= nblk) break;
       const int s = page_of(i) * kBlock + lane;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (r < nr && s <= pos[r]) a.scores[(int64_t)(r0 + r) * a.ld + s] = sbuf[r][u];
+      for (int r = 0; r < R; ++r) {
+        // row offset kept scalar and computed here (hoisted, 16 rows of 64-bit VGPR addresses
+        // would stay live through the whole page loop)
+        int64_t off = (int64_t)(r0 + r) * a.ld;
+        asm volatile("" : "+s"(off));
+        if (r < nr && s <= pos[r]) a.scores[off + s] = sbuf[r][u];
+      }
     }
   }
 
@@ -343,6 +359,10 @@ hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream
     break;
     DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
 #undef DSA_CASE
+    case kPrefillRows:
+      hipLaunchKernelGGL((indexer_rows_kernel<kPrefillRows, KFMT, false>), grid, dim3(kThreads), 0,
+                         s, a);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -359,8 +379,7 @@ hipError_t launch_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s)
     else                                                                                     \
       hipLaunchKernelGGL((indexer_decode_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
     break;
-    DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7)
-    DSA_CASE(8)
+    DSA_CASE(1) DSA_CASE(2)
 #undef DSA_CASE
     default:
       return hipErrorInvalidValue;
@@ -402,20 +421,26 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
                                   : launch_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
 }
 
-// Prefill: the rows of a sequence are cut into tiles of 8 (M = 256 head-rows per MFMA tile
-// column); each workgroup contracts one row tile with one chunk of key pages.  Key pages are
-// re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
+// Prefill: the rows of a sequence are cut into tiles of 16 (queries in LDS); each workgroup
+// contracts one row tile with a long run of key pages, about 2048 workgroups in all.  Key pages
+// are re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
 hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
                                   int32_t max_rows_per_seq, hipStream_t s) {
   IndexerArgs a = a0;
-  constexpr int R = DSA_MAX_ROWS_PER_SEQ;
+  constexpr int R = kPrefillRows;
+  constexpr int kWaves = kThreads / kWave;
   a.tiles_per_seq = (max_rows_per_seq + R - 1) / R;
   a.hist = nullptr;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
   const int64_t gy = (int64_t)a.batch.num_seqs * a.tiles_per_seq;
   if (gy > 65535) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)gy);
-  return launch_rows<DSA_IKEY_FP8>(a, R, grid, s);
+  int64_t chunks = (2048 + gy - 1) / gy;
+  int64_t ppw = (nblk + chunks * kWaves - 1) / (chunks * kWaves);
+  ppw = (ppw + 1) / 2 * 2;
+  if (ppw < 2) ppw = 2;
+  a.pages_per_wave = (int32_t)ppw;
+  dim3 grid((unsigned)((nblk + ppw * kWaves - 1) / (ppw * kWaves)), (unsigned)gy);
+  return launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s);
 }
 
 }  // namespace dsa

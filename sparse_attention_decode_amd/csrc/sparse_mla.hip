@@ -399,8 +399,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
           x[h2][i] = v;
           tmax = fmaxf(tmax, v);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = xor32_max(xor16_max(tmax));
       // Lazy rescaling: the running max only moves when a logit exceeds it by more than 2^4, so
       // probabilities stay <= 16 and O is rarely rescaled.  The fp16 probability times the token
       // scale must stay finite: token (or tensor) scales below 4096.
@@ -422,8 +421,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         for (int i = 0; i < 2; ++i)
           pb[2 * h2 + i] = f16_bits(pv[2 * i]) | (f16_bits(pv[2 * i + 1]) << 16);
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = xor32_sum(xor16_sum(psum));
       l_run = l_run * alpha + psum;
       m_run = m_new;
       const v8h pfrag = __builtin_bit_cast(v8h, uint4{pb[0], pb[1], pb[2], pb[3]});
@@ -487,8 +485,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[mt][0]), fabsf(o[mt][1])),
                                fmaxf(fabsf(o[mt][2]), fabsf(o[mt][3]))));
     amax *= inv;
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = xor32_max(xor16_max(amax));
     if (g == 0) amx[wave][c] = amax;
     lds_barrier();
     amax = fmaxf(amax, amx[wave ^ 1][c]);  // over all 512 dims of the head
