@@ -1,4 +1,4 @@
-// Lightning-indexer scorer for decode and speculative decode.
+// Lightning-indexer scorer: decode, speculative verification and prefill.
 //
 // Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Sparse Attention in K3.1 Pro (every
 // earlier token is scored for each query by 32 light heads over one FP8 key of 132 bytes with its
@@ -9,12 +9,14 @@
 //     score[r,s] = sum_h w[r,h] * ReLU(scale_s * q[r,h] . k[s])
 // computed here as scale_s * sum_h w[r,h] * ReLU(q[r,h] . k[s]) (scale_s > 0).
 //
-// Design (gfx950): the key pages are the only large stream.  A workgroup owns a contiguous chunk
-// of one sequence's blocks; each wave pulls whole 64-token key pages straight from HBM into MFMA
-// operand registers (no LDS staging: each key byte is used by exactly one lane) and scores every
-// row of its sequence from that single read.  The query rows are the MFMA A operand (M = 32 heads
-// per row), keys the B operand (N = 16 tokens per tile, K = 128 dims in one instruction), so the
-// head reduction (ReLU, x w, sum over 32 heads) is 8 lane-local terms plus two cross-lane adds.
+// Design (gfx950): the key pages are the only large stream.  A workgroup owns a long run of one
+// sequence's blocks; each wave pulls whole 64-token key pages straight from HBM into MFMA operand
+// registers (no LDS staging: each key byte is used by exactly one lane) and scores every row of
+// its row tile from that single read.  The query rows are the MFMA A operand (M = 16 heads, two
+// tiles per row), keys the B operand (N = 16 tokens per tile, K = 128 dims in one instruction),
+// so the head reduction (ReLU, x w, sum over 32 heads) is 8 lane-local terms plus two lane-pair
+// adds (permlane swaps).  The 11-bit radix histogram the exact select needs is built on the way
+// (LDS atomics, one global atomic per non-empty bin per workgroup).
 #include "dsa_kernels.h"
 
 namespace dsa {
@@ -22,14 +24,6 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;         // 4 waves
-#ifndef DSA_IDX_PAGES_PER_WAVE
-#define DSA_IDX_PAGES_PER_WAVE 4
-#endif
-#ifndef DSA_IDX_DEPTH
-#define DSA_IDX_DEPTH 1
-#endif
-constexpr int kBlocksPerWave = DSA_IDX_PAGES_PER_WAVE;  // 64-token pages per wave per workgroup
-constexpr int kBlocksPerWG = kBlocksPerWave * (kThreads / kWave);
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
 constexpr int kPrefillRows = 16;      // rows per workgroup tile on the prefill path
 
@@ -62,153 +56,22 @@ __device__ __forceinline__ KeyFrag load_key_frag(const uint8_t* row, const PoolV
   return f;
 }
 
-template <int R, int KFMT, bool HIST>
-__global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a) {
-  __shared__ uint32_t s_hist[HIST ? R * kBins : 1];
-  // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
-  const int seq = blockIdx.y / a.tiles_per_seq;
-  const int tile = blockIdx.y % a.tiles_per_seq;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c = lane & 15;
-
-  const int r0 = a.batch.seq_row_start[seq] + tile * R;
-  const int nr = min(R, a.batch.seq_row_start[seq + 1] - r0);
-  if (nr <= 0) return;
-  int pos[R];
-  int L = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    pos[r] = r < nr ? a.batch.row_pos[r0 + r] : -1;
-    L = max(L, pos[r] + 1);
-  }
-  const int nblk = (L + kBlock - 1) / kBlock;
-  const int blk0 = blockIdx.x * kBlocksPerWG;
-  if (blk0 >= nblk) return;  // whole workgroup past this sequence's end
-
-  constexpr bool use_hist = HIST;
-  if (use_hist) {
-    for (int i = tid; i < R * kBins; i += kThreads) s_hist[i] = 0;
-    __syncthreads();
-  }
-
-  // Query fragments (A operand, FP8 layout) and the head weights of the lane's result rows.
-  v8i qa[R][2];
-  float wv[R][2][4];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = r0 + min(r, max(nr - 1, 0));
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const uint8_t* qr = a.q + ((int64_t)row * DSA_INDEX_HEADS + 16 * mt + c) * DSA_INDEX_DIM;
-      uint4 lo = *reinterpret_cast<const uint4*>(qr + 16 * g);
-      uint4 hi = *reinterpret_cast<const uint4*>(qr + 64 + 16 * g);
-      qa[r][mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y,
-                      (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wv[r][mt][i] = a.w[(int64_t)row * DSA_INDEX_HEADS + 16 * mt + 4 * g + i];
-    }
-  }
-
-  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
-  // Each wave walks its pages (blk0 + wave + 4i) as a software pipeline with D pages in flight:
-  // the operands of page i+D are loading while page i is scored.  Register slots rotate with the
-  // fully unrolled stage index, so every slot is a fixed register range.
-  constexpr int D = R <= 2 ? DSA_IDX_DEPTH : 1;
-  constexpr int S = D + 1;
-  constexpr int kWaves = kThreads / kWave;
-  auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
-  auto load_page = [&](KeyFrag* f, int i) {
-    const int blk = page_of(i);
-    if (i < kBlocksPerWave && blk < nblk) {
-      // the page's pool row is wave-uniform: scalar base, 32-bit lane offsets
-      const uint8_t* row =
-          a.pool.base + (int64_t)__builtin_amdgcn_readfirstlane(bt[blk]) * a.pool.row_bytes;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
-    }
-  };
-  KeyFrag buf[S][4];
-  // Scores stay in registers until the wave's last page has been loaded: loads and stores share
-  // one completion counter, so a store issued between loads would make every later wait for key
-  // data also wait for that store's acknowledgement.
-  float sbuf[R][kBlocksPerWave];
-#pragma unroll
-  for (int i = 0; i < D; ++i) load_page(buf[i], i);
-#pragma unroll
-  for (int base = 0; base < kBlocksPerWave; base += S) {
-    if (page_of(base) >= nblk) break;
-#pragma unroll
-    for (int st = 0; st < S; ++st) {
-      const int i = base + st;
-      load_page(buf[(st + D) % S], i + D);
-      const int blk = page_of(i);
-      if (i >= kBlocksPerWave || blk >= nblk) break;
-      const KeyFrag* cur = buf[st];
-      // After the cross-lane head sum every lane group holds the scores of all four 16-token
-      // tiles; lane group g keeps tile g's, so lane l holds the score of token 64*blk + l.
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (r >= nr) break;
-        float mine = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          v4f z = {0.f, 0.f, 0.f, 0.f};
-          v4f acc0, acc1;
-          if (KFMT == DSA_IKEY_FP8) {
-            acc0 = mfma_fp8(qa[r][0], cur[nt].b, z);
-            acc1 = mfma_fp8(qa[r][1], cur[nt].b, z);
-          } else {
-            acc0 = mfma_fp8_fp4(qa[r][0], cur[nt].b, z, 127, cur[nt].escale);
-            acc1 = mfma_fp8_fp4(qa[r][1], cur[nt].b, z, 127, cur[nt].escale);
-          }
-          float part = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            part += wv[r][0][e] * fmaxf(acc0[e], 0.f);
-            part += wv[r][1][e] * fmaxf(acc1[e], 0.f);
-          }
-          part = xor32_sum(xor16_sum(part));
-          if (g == nt) mine = part * cur[nt].scale;
-        }
-        sbuf[r][i] = mine;
-        if (use_hist && blk * kBlock + lane <= pos[r])
-          atomicAdd(&s_hist[r * kBins + (order_key(mine) >> 21)], 1u);
-      }
-    }
-  }
-  // one coalesced 256-byte store per (page, row)
-#pragma unroll
-  for (int i = 0; i < kBlocksPerWave; ++i) {
-    const int s = page_of(i) * kBlock + lane;
-    if (page_of(i) >= nblk) break;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r < nr && s <= pos[r]) a.scores[(int64_t)(r0 + r) * a.ld + s] = sbuf[r][i];
-  }
-
-  if (use_hist) {
-    __syncthreads();
-    for (int i = tid; i < nr * kBins; i += kThreads) {
-      const uint32_t v = s_hist[i];
-      if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
-    }
-  }
-}
-
-// Several rows per sequence: speculative verification (3..8 rows of one sequence) and prefill
-// (tiles of 16 rows of a chunk).  Same scoring as above, with the rows' queries and head weights
-// in LDS instead of registers (registers for 6-16 rows would leave one wave per SIMD), and each
-// workgroup walking a long run of pages in groups of G (fewer workgroups, so fewer histogram
-// flushes, and every key byte read once per row tile).  Scores leave after each group.
+// One workgroup scores the R query rows of one sequence (decode: 1 row; speculative
+// verification: up to 8; prefill: a tile of 16 rows of the chunk) against a long run of that
+// sequence's key pages, in groups of G pages per wave.  The rows' queries and head weights sit in
+// LDS (registers for 6-16 rows would leave one wave per SIMD).  Long runs mean few workgroups:
+// few histogram flushes, and every key byte is read once per row tile.  Scores stay in registers
+// until the group's last page has been requested (gfx9 has one completion counter for loads and
+// stores), then leave as coalesced 256-byte stores.
 template <int R, int KFMT, bool HIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void indexer_rows_kernel(IndexerArgs a) {
-  constexpr int G = R <= 8 ? 4 : 2;  // pages per store group
+void indexer_kernel(IndexerArgs a) {
+  constexpr int G = R <= 8 ? 4 : 2;   // pages per store group
+  constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
-  __shared__ uint32_t s_hist[HIST ? R * kBins : 1];
+  __shared__ uint32_t s_hist[HIST ? NH * R * kBins : 1];
   // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
   const int seq = blockIdx.y / a.tiles_per_seq;
   const int tile = blockIdx.y % a.tiles_per_seq;
@@ -245,17 +108,28 @@ void indexer_rows_kernel(IndexerArgs a) {
     s_w[i] = a.w[(int64_t)(r0 + min(r, nr - 1)) * DSA_INDEX_HEADS + i % DSA_INDEX_HEADS];
   }
   if (HIST)
-    for (int i = tid; i < R * kBins; i += kThreads) s_hist[i] = 0;
+    for (int i = tid; i < NH * R * kBins; i += kThreads) s_hist[i] = 0;
   __syncthreads();
 
   const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
+  // Block-table entries of this wave's pages, 64 at a time in one lane-distributed register, so a
+  // page's key loads never wait on a table load of their own.
+  int btv = 0, btb = -1;
+  auto row_of = [&](int i) {
+    const int b = i >> 6;
+    if (b != btb) {  // wave-uniform
+      btb = b;
+      const int ii = 64 * b + lane, blk = page_of(ii);
+      btv = (ii < ppw && blk < nblk) ? bt[blk] : 0;
+    }
+    return __builtin_amdgcn_readlane(btv, i & 63);
+  };
   auto load_page = [&](KeyFrag* f, int i) {
     const int blk = page_of(i);
     if (i < ppw && blk < nblk) {
       // the page's pool row is wave-uniform: scalar base, 32-bit lane offsets
-      const uint8_t* row =
-          a.pool.base + (int64_t)__builtin_amdgcn_readfirstlane(bt[blk]) * a.pool.row_bytes;
+      const uint8_t* row = a.pool.base + (int64_t)row_of(i) * a.pool.row_bytes;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
     }
@@ -313,7 +187,7 @@ void indexer_rows_kernel(IndexerArgs a) {
         }
         sbuf[r][u] = mine;
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
-          atomicAdd(&s_hist[r * kBins + (order_key(mine) >> 21)], 1u);
+          atomicAdd(&s_hist[((lane % NH) * R + r) * kBins + (order_key(mine) >> 21)], 1u);
       }
     }
     // one coalesced 256-byte store per (page, row) of the group
@@ -336,7 +210,9 @@ void indexer_rows_kernel(IndexerArgs a) {
   if (HIST) {
     __syncthreads();
     for (int i = tid; i < nr * kBins; i += kThreads) {
-      const uint32_t v = s_hist[i];
+      uint32_t v = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) v += s_hist[h * R * kBins + i];
       if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
     }
   }
@@ -353,34 +229,16 @@ hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream
 #define DSA_CASE(R)                                                                            \
   case R:                                                                                      \
     if (a.hist)                                                                                \
-      hipLaunchKernelGGL((indexer_rows_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
+      hipLaunchKernelGGL((indexer_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
     else                                                                                       \
-      hipLaunchKernelGGL((indexer_rows_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
+      hipLaunchKernelGGL((indexer_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
     break;
-    DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
+    DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
 #undef DSA_CASE
     case kPrefillRows:
-      hipLaunchKernelGGL((indexer_rows_kernel<kPrefillRows, KFMT, false>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false>), grid, dim3(kThreads), 0,
                          s, a);
       break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int KFMT>
-hipError_t launch_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s) {
-  switch (rows) {
-#define DSA_CASE(R)                                                                          \
-  case R:                                                                                    \
-    if (a.hist)                                                                              \
-      hipLaunchKernelGGL((indexer_decode_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
-    else                                                                                     \
-      hipLaunchKernelGGL((indexer_decode_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
-    break;
-    DSA_CASE(1) DSA_CASE(2)
-#undef DSA_CASE
     default:
       return hipErrorInvalidValue;
   }
@@ -402,23 +260,22 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   IndexerArgs a = a0;
   a.tiles_per_seq = 1;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
-  if (rows_per_seq >= 3) {
-    // about 2048 workgroups in all: pages per wave a multiple of 4 in [4, 64]
-    constexpr int kWaves = kThreads / kWave;
-    const int64_t want = (nblk * a.batch.num_seqs + 2047) / 2048;
-    int64_t ppw = (want + kWaves - 1) / kWaves;
-    ppw = (ppw + 3) / 4 * 4;
-    if (ppw < 4) ppw = 4;
-    if (ppw > 64) ppw = 64;
-    a.pages_per_wave = (int32_t)ppw;
-    const int64_t per_wg = ppw * kWaves;
-    dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg), (unsigned)a.batch.num_seqs);
-    return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
-                                    : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
-  }
-  dim3 grid((unsigned)((nblk + kBlocksPerWG - 1) / kBlocksPerWG), (unsigned)a.batch.num_seqs);
-  return ikey_fmt == DSA_IKEY_FP8 ? launch_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
-                                  : launch_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
+  // Workgroups: about 768 (three per CU) for one or two rows, 2048 for more, from the longest
+  // sequence; pages per wave a multiple of 4, at most 16 (one or two rows: ragged batches keep
+  // enough workgroups) or 64.
+  constexpr int kWaves = kThreads / kWave;
+  const int64_t target = rows_per_seq <= 2 ? 768 : 2048;
+  const int64_t cap = rows_per_seq <= 2 ? 16 : 64;
+  const int64_t want = (nblk * a.batch.num_seqs + target - 1) / target;
+  int64_t ppw = (want + kWaves - 1) / kWaves;
+  ppw = (ppw + 3) / 4 * 4;
+  if (ppw < 4) ppw = 4;
+  if (ppw > cap) ppw = cap;
+  a.pages_per_wave = (int32_t)ppw;
+  const int64_t per_wg = ppw * kWaves;
+  dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg), (unsigned)a.batch.num_seqs);
+  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
+                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
 }
 
 // Prefill: the rows of a sequence are cut into tiles of 16 (queries in LDS); each workgroup

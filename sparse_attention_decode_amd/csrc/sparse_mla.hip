@@ -50,7 +50,7 @@ constexpr int kTile = 32;                         // selected tokens per tile
 constexpr int kSteps = DSA_MLA_DQK / 32 / 2;      // 9 K steps of 32 dims per wave (half of 576)
 constexpr int kDvHalf = DSA_MLA_DV / 2;           // 256 output dims per wave
 #ifndef DSA_MLA_STAGES
-#define DSA_MLA_STAGES 4
+#define DSA_MLA_STAGES 3
 #endif
 // Gather pipeline: while tile j is processed, tiles j+1 .. j+kAhead are in flight.
 constexpr int kStages = DSA_MLA_STAGES;
