@@ -126,15 +126,16 @@ DSA_API dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, i
  *   w      [num_rows][32] fp32 head weights
  *   scores [num_rows][ld_scores] fp32 output; entries [0, row_pos[r]] are written, the rest are
  *          left untouched.  ld_scores >= max_context.
- *   hist   [num_rows][DSA_HIST_BINS] uint32 in/out or NULL: counts of the top 11 bits of each
- *          written score's order-preserving key are added to it; dsa_topk consumes it (saving a
- *          pass over the scores) and returns it to zero.  It must be all zero on entry: allocate
- *          it zeroed once, and clear it yourself if scores are computed without a dsa_topk call.
- *          Only available on the decode path (max_rows_per_seq <= 8); must be NULL otherwise.
+ *   hist   [num_rows][DSA_HIST_BINS] uint32 in/out or NULL (4-byte aligned): counts of the top
+ *          11 bits of each written score's order-preserving key are added to it; dsa_topk
+ *          consumes it (saving a pass over the scores) and returns it to zero.  It must be all
+ *          zero on entry: allocate it zeroed once, and clear it yourself if scores are computed
+ *          without a dsa_topk call.  Only available on the decode path (max_rows_per_seq <= 8);
+ *          must be NULL otherwise.
  * Decode and speculative decode (max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ) stream the index keys
  * once per sequence and score all of that sequence's rows from each key read.  Prefill chunks
- * (more rows per sequence; FP8 keys only) run as a dense FP8 matrix contraction of row tiles
- * against key tiles.
+ * (more rows per sequence; FP8 keys only) score tiles of 16 rows, streaming each key page once per
+ * tile.
  * Exactness: key products are exact and accumulate in fp32; scale_s > 0 is applied after the
  * head sum (equal to applying it inside each ReLU whenever the sums are exact).
  */

@@ -199,6 +199,7 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   if (ld_scores < batch->max_context)
     return fail(DSA_ERR_INVALID_ARG, "ld_scores %lld < max_context %lld", (long long)ld_scores,
                 (long long)batch->max_context);
+  if (hist && !aligned(hist, 4)) return fail(DSA_ERR_INVALID_ARG, "hist must be 4-byte aligned");
   if (batch->num_rows == 0) return DSA_OK;
   dsa::IndexerArgs a;
   a.pool = pool_view(kv, pool);
@@ -239,6 +240,7 @@ dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float
   if (batch->max_context > (int64_t)dsa::kMaxSlices * dsa::kTopkSlice)
     return fail(DSA_ERR_UNSUPPORTED, "top-k is built for contexts up to %d tokens",
                 dsa::kMaxSlices * dsa::kTopkSlice);
+  if (hist && !aligned(hist, 4)) return fail(DSA_ERR_INVALID_ARG, "hist must be 4-byte aligned");
   if (phys) {
     if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is required for phys rows");
     if (kv->block_size != 64) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
