@@ -37,6 +37,12 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Workgroup barrier over LDS only: waits for this wave's LDS operations, not its global loads or
+// stores (__syncthreads waits for those too).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // 16x16x128 FP8 x FP8 MFMA (E4M3 operands, fp32 accumulate).  Operand layout, lane l,
 // group g = l / 16: row/col l % 16; bytes 0..15 hold K [16g, 16g+16), bytes 16..31 hold
 // K [64+16g, 64+16g+16).  Result lane l: rows 4g..4g+3, col l % 16.

@@ -26,6 +26,8 @@ namespace {
 constexpr int kThreads = 256;         // 4 waves
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
 constexpr int kPrefillRows = 16;      // rows per workgroup tile on the prefill path
+constexpr int kMaxPagesPerWave = 64;  // one block-table entry per lane
+constexpr int kMaxPagesSmallR = 16;   // one or two rows: the whole run's scores in registers
 
 // Operand fragments of one 16-token tile.
 struct KeyFrag {
@@ -34,41 +36,77 @@ struct KeyFrag {
   float scale; // FP8: scale_s of the lane's token
 };
 
+// Byte offsets, within a pool row, of what lane (g, c) reads for token c of a page's first
+// 16-token tile (tile nt adds nt * 16 tokens).
+struct LaneOffsets {
+  int key, scale;
+};
+
 template <int KFMT>
-__device__ __forceinline__ KeyFrag load_key_frag(const uint8_t* row, const PoolView& p, int n,
-                                                 int g) {
-  KeyFrag f;
+__device__ __forceinline__ LaneOffsets lane_offsets(const PoolView& p, int g, int c) {
+  LaneOffsets o;
   if (KFMT == DSA_IKEY_FP8) {
-    const uint8_t* k = row + p.ikey_off + n * DSA_INDEX_DIM;
-    uint4 lo = *reinterpret_cast<const uint4*>(k + 16 * g);
-    uint4 hi = *reinterpret_cast<const uint4*>(k + 64 + 16 * g);
-    f.b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-              (int)hi.w};
-    f.scale = *reinterpret_cast<const float*>(row + p.ikey_scale_off + n * 4);
-    f.escale = 127;
+    o.key = (int)p.ikey_off + c * DSA_INDEX_DIM + 16 * g;
+    o.scale = (int)p.ikey_scale_off + c * 4;
   } else {
-    const uint8_t* k = row + p.ikey_off + n * (DSA_INDEX_DIM / 2);
-    uint4 v = *reinterpret_cast<const uint4*>(k + 16 * g);
-    f.b = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-    f.escale = row[p.ikey_scale_off + n * 4 + g];
-    f.scale = 1.0f;
+    o.key = (int)p.ikey_off + c * (DSA_INDEX_DIM / 2) + 16 * g;
+    o.scale = (int)p.ikey_scale_off + c * 4 + g;
   }
-  return f;
+  return o;
+}
+
+// A buffer resource over one pool row.  A page that does not exist (past the wave's run or the
+// sequence) gets zero records: its loads are still issued, return zeros and touch no memory, so
+// the compiler can count every outstanding page load and keep exactly one page in flight behind
+// the one being scored.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(row), (short)0, bytes,
+                                           0x00020000 /* gfx9: 32-bit data format */);
+}
+
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
+template <int KFMT>
+__device__ __forceinline__ void load_key_page(KeyFrag* f, __amdgpu_buffer_rsrc_t rs,
+                                              const LaneOffsets& o) {
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    if (KFMT == DSA_IKEY_FP8) {
+      const int k = o.key + nt * 16 * DSA_INDEX_DIM;
+      const uint4 lo = ld16(rs, k), hi = ld16(rs, k + 64);
+      f[nt].b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                    (int)hi.w};
+      f[nt].scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.scale + nt * 64, 0, 0));
+      f[nt].escale = 127;
+    } else {
+      const uint4 v = ld16(rs, o.key + nt * 16 * (DSA_INDEX_DIM / 2));
+      f[nt].b = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      f[nt].escale = __builtin_amdgcn_raw_buffer_load_b8(rs, o.scale + nt * 64, 0, 0);
+      f[nt].scale = 1.0f;
+    }
+  }
 }
 
 // One workgroup scores the R query rows of one sequence (decode: 1 row; speculative
-// verification: up to 8; prefill: a tile of 16 rows of the chunk) against a long run of that
-// sequence's key pages, in groups of G pages per wave.  The rows' queries and head weights sit in
-// LDS (registers for 6-16 rows would leave one wave per SIMD).  Long runs mean few workgroups:
-// few histogram flushes, and every key byte is read once per row tile.  Scores stay in registers
-// until the group's last page has been requested (gfx9 has one completion counter for loads and
-// stores), then leave as coalesced 256-byte stores.
+// verification: up to 8; prefill: a tile of 16 rows of the chunk) against a run of that
+// sequence's key pages (at most 64 per wave).  The rows' queries and head weights sit in LDS
+// (registers for 6-16 rows would leave one wave per SIMD).  Every key byte is read once per row
+// tile.  Scores stay in registers for G pages and then leave as coalesced 256-byte streaming
+// stores: for one or two rows G covers the whole run, so no store is pending while page loads are
+// (gfx9 counts loads and stores on one counter, and a mix makes every later wait a full drain).
 template <int R, int KFMT, bool HIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_kernel(IndexerArgs a) {
-  constexpr int G = R <= 8 ? 4 : 2;   // pages per store group
+  constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
+  constexpr int kQChunks = R * DSA_INDEX_HEADS * (DSA_INDEX_DIM / 16);  // 16-byte pieces
+  constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
+  constexpr int kWPer = (R * DSA_INDEX_HEADS + kThreads - 1) / kThreads;
+  constexpr int kWaves = kThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? NH * R * kBins : 1];
@@ -82,6 +120,33 @@ void indexer_kernel(IndexerArgs a) {
   const int r0 = __builtin_amdgcn_readfirstlane(a.batch.seq_row_start[seq] + tile * R);
   const int nr = __builtin_amdgcn_readfirstlane(min(R, a.batch.seq_row_start[seq + 1] - r0));
   if (nr <= 0) return;
+  const int ppw = a.pages_per_wave;  // <= 64: one block-table entry per lane
+  const int blk0 = blockIdx.x * kWaves * ppw;
+
+  // Loads that need only the sequence and the rows, issued together before the row positions are
+  // read: the block-table entry of this wave's page `lane` (first, so the first page waits for it
+  // alone; clamped into the table's row, unused lanes are discarded below), the rows' queries and
+  // their head weights (rows past nr repeat the last row; their results are never used).
+  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
+  const int my_blk = blk0 + wave + kWaves * lane;
+  const int bt_raw = bt[min((int64_t)my_blk, a.batch.ld_bt - 1)];
+  uint4 qv[kQPer];
+  float wl[kWPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = min(tid + kThreads * j, kQChunks - 1);
+    const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
+    const int r = rh / DSA_INDEX_HEADS, h = rh % DSA_INDEX_HEADS;
+    const int row = r0 + min(r, nr - 1);
+    qv[j] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)row * DSA_INDEX_HEADS + h) * DSA_INDEX_DIM + 16 * ch);
+  }
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const int i = min(tid + kThreads * j, R * DSA_INDEX_HEADS - 1);
+    const int r = i / DSA_INDEX_HEADS;
+    wl[j] = a.w[(int64_t)(r0 + min(r, nr - 1)) * DSA_INDEX_HEADS + i % DSA_INDEX_HEADS];
+  }
+  asm volatile("" ::: "memory");  // not to be sunk below the early exit
   int pos[R];
   int L = 0;
 #pragma unroll
@@ -90,60 +155,48 @@ void indexer_kernel(IndexerArgs a) {
     L = max(L, pos[r] + 1);
   }
   const int nblk = (L + kBlock - 1) / kBlock;
-  constexpr int kWaves = kThreads / kWave;
-  const int ppw = a.pages_per_wave;
-  const int blk0 = blockIdx.x * kWaves * ppw;
-  if (blk0 >= nblk) return;
-
-  // queries (rows past nr repeat the last row; their results are never used) and weights
-  for (int i = tid; i < R * DSA_INDEX_HEADS * (DSA_INDEX_DIM / 16); i += kThreads) {
-    const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
-    const int r = rh / DSA_INDEX_HEADS, h = rh % DSA_INDEX_HEADS;
-    const int row = r0 + min(r, nr - 1);
-    *reinterpret_cast<uint4*>(&s_q[rh * kQRow + 16 * ch]) =
-        *reinterpret_cast<const uint4*>(a.q + ((int64_t)row * DSA_INDEX_HEADS + h) * DSA_INDEX_DIM + 16 * ch);
+  if (blk0 >= nblk) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
   }
-  for (int i = tid; i < R * DSA_INDEX_HEADS; i += kThreads) {
-    const int r = i / DSA_INDEX_HEADS;
-    s_w[i] = a.w[(int64_t)(r0 + min(r, nr - 1)) * DSA_INDEX_HEADS + i % DSA_INDEX_HEADS];
+  // lane j: pool row of this wave's page j, or -1 where that page does not exist
+  const int64_t pool_rows = a.pool.tokens / kBlock;
+  const int btv = (lane < ppw && my_blk < nblk && bt_raw >= 0 && bt_raw < pool_rows) ? bt_raw : -1;
+  auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
+  const int row_bytes = (int)a.pool.row_bytes;
+  auto page_rsrc = [&](int i) {
+    const int prow = __builtin_amdgcn_readlane(btv, i & 63);
+    const bool ok = i < ppw && prow >= 0;  // wave-uniform
+    return row_rsrc(a.pool.base + (int64_t)(ok ? prow : 0) * row_bytes, ok ? row_bytes : 0);
+  };
+  const LaneOffsets lo = lane_offsets<KFMT>(a.pool, g, c);
+  KeyFrag buf[2][4];
+  load_key_page<KFMT>(buf[0], page_rsrc(0), lo);
+
+  // queries and weights to LDS (the first page is on its way meanwhile)
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = tid + kThreads * j;
+    if (i < kQChunks) {
+      const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
+      *reinterpret_cast<uint4*>(&s_q[rh * kQRow + 16 * ch]) = qv[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const int i = tid + kThreads * j;
+    if (i < R * DSA_INDEX_HEADS) s_w[i] = wl[j];
   }
   if (HIST)
     for (int i = tid; i < NH * R * kBins; i += kThreads) s_hist[i] = 0;
-  __syncthreads();
+  lds_barrier();  // not a wait for the first page: the second is requested before that
 
-  const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
-  auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
-  // Block-table entries of this wave's pages, 64 at a time in one lane-distributed register, so a
-  // page's key loads never wait on a table load of their own.
-  int btv = 0, btb = -1;
-  auto row_of = [&](int i) {
-    const int b = i >> 6;
-    if (b != btb) {  // wave-uniform
-      btb = b;
-      const int ii = 64 * b + lane, blk = page_of(ii);
-      btv = (ii < ppw && blk < nblk) ? bt[blk] : 0;
-    }
-    return __builtin_amdgcn_readlane(btv, i & 63);
-  };
-  auto load_page = [&](KeyFrag* f, int i) {
-    const int blk = page_of(i);
-    if (i < ppw && blk < nblk) {
-      // the page's pool row is wave-uniform: scalar base, 32-bit lane offsets
-      const uint8_t* row = a.pool.base + (int64_t)row_of(i) * a.pool.row_bytes;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) f[nt] = load_key_frag<KFMT>(row, a.pool, 16 * nt + c, g);
-    }
-  };
-  KeyFrag buf[2][4];
-  load_page(buf[0], 0);
-#pragma unroll 1
-  for (int i0 = 0; i0 < ppw; i0 += G) {
-    if (page_of(i0) >= nblk) break;
-    float sbuf[R][G];
+  // Scores of the group of G pages starting at page i0 into sbuf (and the histogram).
+  auto score_group = [&](int i0, float (&sbuf)[R][G]) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
-      load_page(buf[(u + 1) & 1], i + 1);
+      load_key_page<KFMT>(buf[(u + 1) & 1], page_rsrc(i + 1), lo);  // always issued
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const int blk = page_of(i);
@@ -157,10 +210,10 @@ void indexer_kernel(IndexerArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const uint8_t* qr = &s_q[(r * DSA_INDEX_HEADS + 16 * mt + c) * kQRow];
-          const uint4 lo = *reinterpret_cast<const uint4*>(qr + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(qr + 64 + 16 * g);
-          qa[mt] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                       (int)hi.w};
+          const uint4 ql = *reinterpret_cast<const uint4*>(qr + 16 * g);
+          const uint4 qh = *reinterpret_cast<const uint4*>(qr + 64 + 16 * g);
+          qa[mt] = v8i{(int)ql.x, (int)ql.y, (int)ql.z, (int)ql.w, (int)qh.x, (int)qh.y, (int)qh.z,
+                       (int)qh.w};
           const float4 w4 = *reinterpret_cast<const float4*>(&s_w[r * DSA_INDEX_HEADS + 16 * mt + 4 * g]);
           wv[mt][0] = w4.x; wv[mt][1] = w4.y; wv[mt][2] = w4.z; wv[mt][3] = w4.w;
         }
@@ -185,12 +238,17 @@ void indexer_kernel(IndexerArgs a) {
           part = xor32_sum(xor16_sum(part));
           if (g == nt) mine = part * cur[nt].scale;
         }
+        // materialise the score here: left to the store, the page's whole computation (pure)
+        // would be sunk there and every page's key fragments would stay live until then
+        asm volatile("" : "+v"(mine));
         sbuf[r][u] = mine;
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
           atomicAdd(&s_hist[((lane % NH) * R + r) * kBins + (order_key(mine) >> 21)], 1u);
       }
     }
-    // one coalesced 256-byte store per (page, row) of the group
+  };
+  // One coalesced 256-byte streaming store per (page, row) of the group starting at page i0.
+  auto store_group = [&](int i0, const float (&sbuf)[R][G]) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
@@ -202,19 +260,36 @@ void indexer_kernel(IndexerArgs a) {
         // would stay live through the whole page loop)
         int64_t off = (int64_t)(r0 + r) * a.ld;
         asm volatile("" : "+s"(off));
-        if (r < nr && s <= pos[r]) a.scores[off + s] = sbuf[r][u];
+        if (r < nr && s <= pos[r]) __builtin_nontemporal_store(sbuf[r][u], &a.scores[off + s]);
       }
     }
-  }
-
-  if (HIST) {
-    __syncthreads();
+  };
+  auto flush_hist = [&]() {
+    lds_barrier();  // every wave's LDS counts are in; its global stores need not be
     for (int i = tid; i < nr * kBins; i += kThreads) {
       uint32_t v = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h) v += s_hist[h * R * kBins + i];
       if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
     }
+  };
+
+  if constexpr (G == kMaxPagesSmallR) {
+    // The whole run is one group (pages per wave <= G): the histogram flush goes out before the
+    // stores and neither waits for the other, so the kernel's tail is one round trip.
+    float sbuf[R][G];
+    score_group(0, sbuf);
+    if (HIST) flush_hist();
+    store_group(0, sbuf);
+  } else {
+#pragma unroll 1
+    for (int i0 = 0; i0 < ppw; i0 += G) {
+      if (page_of(i0) >= nblk) break;
+      float sbuf[R][G];
+      score_group(i0, sbuf);
+      store_group(i0, sbuf);
+    }
+    if (HIST) flush_hist();
   }
 }
 
@@ -261,11 +336,11 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   a.tiles_per_seq = 1;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
   // Workgroups: about 768 (three per CU) for one or two rows, 2048 for more, from the longest
-  // sequence; pages per wave a multiple of 4, at most 16 (one or two rows: ragged batches keep
-  // enough workgroups) or 64.
+  // sequence; pages per wave a multiple of 4, at most 16 (one or two rows: the run's scores stay
+  // in registers, and ragged batches keep enough workgroups) or 64.
   constexpr int kWaves = kThreads / kWave;
   const int64_t target = rows_per_seq <= 2 ? 768 : 2048;
-  const int64_t cap = rows_per_seq <= 2 ? 16 : 64;
+  const int64_t cap = rows_per_seq <= 2 ? kMaxPagesSmallR : kMaxPagesPerWave;
   const int64_t want = (nblk * a.batch.num_seqs + target - 1) / target;
   int64_t ppw = (want + kWaves - 1) / kWaves;
   ppw = (ppw + 3) / 4 * 4;
@@ -279,7 +354,8 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
 }
 
 // Prefill: the rows of a sequence are cut into tiles of 16 (queries in LDS); each workgroup
-// contracts one row tile with a long run of key pages, about 2048 workgroups in all.  Key pages
+// contracts one row tile with a run of at most 64 key pages per wave, at least about 2048
+// workgroups in all.  Key pages
 // are re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
 hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
                                   int32_t max_rows_per_seq, hipStream_t s) {
@@ -295,6 +371,7 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
   int64_t ppw = (nblk + chunks * kWaves - 1) / (chunks * kWaves);
   ppw = (ppw + 1) / 2 * 2;
   if (ppw < 2) ppw = 2;
+  if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
   a.pages_per_wave = (int32_t)ppw;
   dim3 grid((unsigned)((nblk + ppw * kWaves - 1) / (ppw * kWaves)), (unsigned)gy);
   return launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s);

@@ -92,12 +92,6 @@ struct Stage {
   int32_t* valid;  // [kTile] slot holds a selected, visible token
 };
 
-// Workgroup barrier over LDS only: waits for this wave's LDS operations, not its global loads
-// (those are waited for explicitly, per stage).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Position of tile token t (quad q = t / 4, u = t % 4) in a dim-major row: the K slot that holds
 // it in the PV contraction.
 __device__ __forceinline__ int vt_pos(int t) {
