@@ -57,6 +57,7 @@ constexpr int kStages = DSA_MLA_STAGES;
 constexpr int kAhead = kStages - 1;
 static_assert(kStages >= 3 && kStages <= 6, "stage variables raw0..raw5");
 constexpr int kRowsPerWave = (kTile + kWavesM - 1) / kWavesM;  // 3 (rows >= 32 are dummies)
+constexpr int kSlots = kRowsPerWave * kWavesM;                  // 36 LDS rows per stage
 // Pool rows of a wave's gathers, one register per batch of tiles: lane 3T + r holds the row of
 // tile T's row r of the batch (kBatchTiles tiles per register).
 constexpr int kBatchTiles = kWave / kRowsPerWave;  // 21
@@ -87,10 +88,35 @@ struct Geo {
 // __shared__ variables, so the compiler can tell the reads of one stage from the gathers still
 // landing in the others (one shared array would make it wait for every gather before any read).
 struct Stage {
-  uint8_t* raw;    // [kTile][kRaw] latent rows as stored
-  float* tsc;      // [kTile] FP8 token scales
+  uint8_t* raw;    // [kSlots][kRaw] latent rows as stored (rows >= kTile: dummy gathers)
+  float* tsc;      // [kSlots] FP8 token scales
   int32_t* valid;  // [kTile] slot holds a selected, visible token
 };
+
+// The value of x, opaque to the optimiser: lane-dependent addresses derived from it inside the tile
+// loop are recomputed each tile (a few VALU) instead of being hoisted out of the loop, where they
+// would hold registers for the whole loop and push the kernel into spills.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Direct global->LDS copies.  Lane l copies `bytes` bytes from src + voff (src wave-uniform) to LDS
+// address lds + bytes * l.  Issued through inline assembly, so the compiler does not track them:
+// the tile loop waits for them explicitly (s_waitcnt vmcnt by count, then an LDS barrier).  Left
+// to the compiler, its LDS-DMA tracking made some LDS writes wait for every copy in flight, which
+// undid the gather pipeline.  Untracked copies only ever make the compiler's own waits stricter.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+__device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
+}
 
 // Position of tile token t (quad q = t / 4, u = t % 4) in a dim-major row: the K slot that holds
 // it in the PV contraction.
@@ -101,53 +127,47 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 // Issue the direct global->LDS gathers of tile j (selected slots [j, min(j+32, jend))) into stage
 // st.  Wave w gathers tile rows w, w+12, w+24, whose pool rows are lanes lb, lb+1, lb+2 of `pv`.
-// Rows past the tile and slots without a token gather a dummy into `junk`, so that every wave
-// issues kGathersPerWave loads per tile: the wave's first real row of the tile again if it has
-// one, else a pool row that depends on the workgroup and wave (never one row for everybody:
-// thousands of requests to one address would queue on one memory channel).
+// Rows past the tile (slots 32..35 of the stage) and slots without a token gather a dummy row,
+// so that every wave issues kGathersPerWave loads per tile: the wave's first real row of the
+// tile again if it has one, else `ph_spread`, a pool row that depends on the workgroup and wave
+// (never one row for everybody: thousands of requests to one address would queue on one memory
+// channel).  Every gather lands in the stage's own LDS variable, and its pool row is
+// wave-uniform (scalar base address, 32-bit lane offset).
 template <int LFMT>
-__device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, uint8_t* junk,
-                                           const MlaArgs& a, int j, int jend) {
+__device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int ph_spread,
+                                           const MlaArgs& a, int j, int jend, int lane) {
   using G = Geo<LFMT>;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ph_first = (j + wave < jend) ? __builtin_amdgcn_readlane(pv, lb) : -1;
-  const int ph_spread =
-      (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens);
   const int ph_dummy = ph_first >= 0 ? ph_first : ph_spread;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int t = wave + kWavesM * r;
+    const int t = wave + kWavesM * r;  // < kSlots
     const int jj = j + t;
     const int ph = (t < kTile && jj < jend) ? __builtin_amdgcn_readlane(pv, lb + r) : -1;
     if (t < kTile && lane == 0) st.valid[t] = ph >= 0;
-    const int src = ph >= 0 ? ph : ph_dummy;
-    const uint8_t* row = a.pool.base + (int64_t)(src / kBlock) * a.pool.row_bytes;
-    const int slot = src % kBlock;
-    uint8_t* dst = t < kTile ? st.raw + t * G::kRaw : junk;
+    const int src = __builtin_amdgcn_readfirstlane(ph >= 0 ? ph : ph_dummy);  // >= 0
+    const uint8_t* row = a.pool.base + (int64_t)(src >> 6) * a.pool.row_bytes;
+    const int slot = src & (kBlock - 1);
+    uint8_t* dst = st.raw + t * G::kRaw;
     if constexpr (G::kFp8) {
-      float* dsc = t < kTile ? st.tsc + t : reinterpret_cast<float*>(junk + kRaw8);
-      if (lane < DSA_MLA_DQK / 16)
-        __builtin_amdgcn_global_load_lds(row + a.pool.lat_off + slot * DSA_MLA_DQK + 16 * lane,
-                                         (lds_void*)dst, 16, 0, 0);
-      if (lane == 0)
-        __builtin_amdgcn_global_load_lds(row + a.pool.lat_scale_off + slot * 4, (lds_void*)dsc,
-                                         4, 0, 0);
+      const uint8_t* lat = row + a.pool.lat_off + slot * DSA_MLA_DQK;
+      const uint8_t* scl = row + a.pool.lat_scale_off + slot * 4;
+      if (lane < DSA_MLA_DQK / 16) lds_copy16(lat, 16 * lane, lds_addr(dst));
+      if (lane == 0) lds_copy4(scl, 0, lds_addr(st.tsc + t));
     } else {
-      if (lane < DSA_MLA_DQK / 32)
-        __builtin_amdgcn_global_load_lds(row + a.pool.lat_off + slot * (DSA_MLA_DQK / 2) + 16 * lane,
-                                         (lds_void*)dst, 16, 0, 0);
-      if (lane < DSA_MLA_DQK / 64)
-        __builtin_amdgcn_global_load_lds(
-            row + a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16) + 4 * lane,
-            (lds_void*)(dst + DSA_MLA_DQK / 2), 4, 0, 0);
+      const uint8_t* lat = row + a.pool.lat_off + slot * (DSA_MLA_DQK / 2);
+      const uint8_t* scl = row + a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16);
+      if (lane < DSA_MLA_DQK / 32) lds_copy16(lat, 16 * lane, lds_addr(dst));
+      if (lane < DSA_MLA_DQK / 64) lds_copy4(scl, 4 * lane, lds_addr(dst + DSA_MLA_DQK / 2));
     }
   }
 }
 
 // FP8: dim-major copy of the value dims of a stage (bytes, transposed in 4x4 blocks); tokens that
 // are not selected get zeros so that their (zero) probabilities never meet stale data.
-__device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt) {
-  for (int blk = threadIdx.x; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
+__device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid) {
+  for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
     const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
     uint32_t w[4];
 #pragma unroll
@@ -172,8 +192,8 @@ __device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt) {
 
 // NVFP4: decode a stage once into the bf16 token-major tile and the fp16 dim-major tile (E2M1 x
 // E4M3 products are exact in both).
-__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* vt) {
-  for (int it = threadIdx.x; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
+__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* vt, int tid) {
+  for (int it = tid; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
     const int t = it & 31, blk = it >> 5;  // token, 16-dim block
     float v[16];
     if (st.valid[t]) {
@@ -246,22 +266,22 @@ __device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int g) {
   }
 }
 
-template <int LFMT>
+// PHYS: the select's physical pool rows are given (else selected indices + block table).
+template <int LFMT, bool PHYS>
 __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   using G = Geo<LFMT>;
-  constexpr int kRawBytes = kTile * G::kRaw;
+  constexpr int kRawBytes = kSlots * G::kRaw;
   __shared__ __attribute__((aligned(16))) uint8_t raw0[kRawBytes], raw1[kRawBytes], raw2[kRawBytes];
   __shared__ __attribute__((aligned(16))) uint8_t raw3[kStages > 3 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw4[kStages > 4 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw5[kStages > 5 ? kRawBytes : 16];
-  __shared__ float tsc0[kTile], tsc1[kTile], tsc2[kTile], tsc3[kTile], tsc4[kTile], tsc5[kTile];
+  __shared__ float tsc0[kSlots], tsc1[kSlots], tsc2[kSlots], tsc3[kSlots], tsc4[kSlots], tsc5[kSlots];
   __shared__ int32_t valid0[kTile], valid1[kTile], valid2[kTile], valid3[kTile], valid4[kTile],
       valid5[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
   __shared__ __attribute__((aligned(16))) v4f sx[kWavesM][2][kWave];  // partial S^T exchange
   __shared__ float amx[kWavesM][16];
-  __shared__ __attribute__((aligned(16))) uint8_t junk[G::kRaw + 16];  // dummy gathers land here
   const Stage stages[6] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2},
                            {raw3, tsc3, valid3}, {raw4, tsc4, valid4}, {raw5, tsc5, valid5}};
 
@@ -273,12 +293,12 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   const int head = 16 * (wave >> 1) + c;  // this lane's head in S^T / O^T columns
 
   const int32_t* idx = a.idx + (int64_t)row * a.k;
-  const int32_t* prow = a.phys ? a.phys + (int64_t)row * a.k : nullptr;
+  const int32_t* prow = a.phys + (int64_t)row * a.k;
   const int nvis = a.batch.row_pos[row] + 1;  // selected indices outside [0, nvis) are ignored
   const int j0 = split * a.tokens_per_split;
   const int j1 = min(a.k, j0 + a.tokens_per_split);
   const int32_t* bt = nullptr;
-  if (!prow) {  // sequence of the row, by one ballot per 64 sequences
+  if (!PHYS) {  // sequence of the row, by one ballot per 64 sequences
     int seq = 0;
     for (int b0 = 0; b0 < a.batch.num_seqs; b0 += kWave) {
       const int b = b0 + lane;
@@ -291,28 +311,31 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   // Pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane 3T + r:
   // tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  // dummy gather row of this wave when a tile has no real row for it (see issue_tile)
+  const int ph_spread = __builtin_amdgcn_readfirstlane(
+      (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens));
   auto load_batch = [&](int tb) {
     const int T = lane / kRowsPerWave, r = lane % kRowsPerWave;
     const int t = wave + kWavesM * r;
     const int jj = j0 + kTile * (tb + T) + t;
+    const bool in = T < kBatchTiles && t < kTile && jj < j1;
     int ph = -1;
-    if (T < kBatchTiles && t < kTile && jj < j1) {
-      if (prow) {
-        ph = prow[jj];
-        if (ph >= a.pool.tokens) ph = -1;
-      } else {
-        const int s = idx[jj];
-        ph = (s >= 0 && s < nvis) ? bt[s / kBlock] * kBlock + (s % kBlock) : -1;
-      }
+    if (PHYS) {
+      // unconditional (entry 0 stands in for lanes without a slot), so that the query loads
+      // behind it are in flight at the same time
+      const int jc = in ? jj : 0;
+      const int v = *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(prow) +
+                                                      (uint32_t)(4 * jc));  // scalar base
+      ph = (in && v < a.pool.tokens) ? v : -1;
+    } else if (in) {
+      const int s = idx[jj];
+      ph = (s >= 0 && s < nvis) ? bt[s / kBlock] * kBlock + (s % kBlock) : -1;
     }
     return ph;
   };
 
-  // Prologue: the pool rows of the first batches are loaded first (the gathers wait for them);
-  // the query loads are issued right behind them and complete under the first gathers.
-  int tb = 0;
-  int pv = load_batch(0);
-  int pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : -1;
+  // Prologue: the query loads go first (unconditional), the pool rows of the first batches right
+  // behind them, so both round trips overlap.
   // Q^T fragments (B operand) of this wave's half of the contraction
   const int kd = kHalfDims * dh;  // first dim of the half (wave-uniform)
   v8bf qf[kSteps];
@@ -322,15 +345,19 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     for (int i = 0; i < kSteps; ++i)
       qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 32 * i));
   }
-  if (ntiles > 0) issue_tile<LFMT>(stages[0], pv, 0, junk, a, j0, j1);
-  // Consume the query registers between the first two tiles' gathers: the compiler cannot count
-  // the gathers (they sit behind lane conditions), so its wait for the query is a full wait; here
-  // that covers the query and tile 0 only, and keeps it out of the loop.
+  asm volatile("" ::: "memory");  // keep the query loads ahead of the pool-row loads
+  int tb = 0;
+  int pv = load_batch(0);
+  int pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : -1;
+  // The pool rows and the query arrive together (one wait, before the first gather is issued:
+  // the gathers are invisible to the compiler, and a wait of its own behind them would be a full
+  // drain of the pipeline).
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) asm volatile("" ::"v"(qf[i]));
+  for (int i = 0; i < kSteps; ++i) asm volatile("" ::"v"(qf[i]), "v"(pv), "v"(pv_next));
 #pragma unroll
-  for (int T = 1; T < kAhead; ++T)
-    if (T < ntiles) issue_tile<LFMT>(stages[T], pv, kRowsPerWave * T, junk, a, j0 + T * kTile, j1);
+  for (int T = 0; T < kAhead; ++T)
+    if (T < ntiles)
+      issue_tile<LFMT>(stages[T], pv, kRowsPerWave * T, ph_spread, a, j0 + T * kTile, j1, lane);
 
   v4f o[kDvHalf / 16];
 #pragma unroll
@@ -356,10 +383,12 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
+      const int tl = opaque((int)threadIdx.x);
+      const int ln = tl & 63, gl = ln >> 4, cl = ln & 15;
       if constexpr (G::kFp8)
-        build_fp8(cur, vt);
+        build_fp8(cur, vt, tl);
       else
-        build_nvfp4(cur, ct, vt);
+        build_nvfp4(cur, ct, vt, tl);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
       // this wave's half of S^T (tokens x heads) for the two 16-token halves of the tile
@@ -369,13 +398,13 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kSteps; ++i)
-          acc = mfma_bf16(qk_operand<LFMT>(cur, ct, 16 * h2 + c, kd + 32 * i + 8 * g), qf[i], acc);
+          acc = mfma_bf16(qk_operand<LFMT>(cur, ct, 16 * h2 + cl, kd + 32 * i + 8 * gl), qf[i], acc);
         sfr[h2] = acc;
-        sx[wave][h2][lane] = acc;
+        sx[wave][h2][ln] = acc;
       }
       lds_barrier();  // partial S^T of both halves, and the value tile, are in LDS
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) sfr[h2] += sx[wave ^ 1][h2][lane];
+      for (int h2 = 0; h2 < 2; ++h2) sfr[h2] += sx[wave ^ 1][h2][ln];
 
       // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head
       float x[2][4], ts[2][4];
@@ -384,7 +413,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = 16 * h2 + 4 * g + i;
+          const int t = 16 * h2 + 4 * gl + i;
           const bool ok = cur.valid[t];
           // stale LDS bits of slots without a token are never used
           const float scl = ok ? (G::kFp8 ? cur.tsc[t] : a.tensor_scale) : 0.f;
@@ -427,7 +456,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // O^T (dims x heads) += V^T P^T; A operand lane: dim 256dh + 16mt + c, K slots 8g .. 8g+7
 #pragma unroll
       for (int mt = 0; mt < kDvHalf / 16; ++mt)
-        o[mt] = mfma_f16(pv_operand<LFMT>(vt, kDvHalf * dh + 16 * mt + c, g), pfrag, o[mt]);
+        o[mt] = mfma_f16(pv_operand<LFMT>(vt, kDvHalf * dh + 16 * mt + cl, gl), pfrag, o[mt]);
 
       // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
       // first barrier, so no one reads it any more).  Issued last: a wave that finds the gather
@@ -440,8 +469,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
           if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
         }
         if (T < ntiles)
-          issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, kRowsPerWave * (T - tb), junk, a,
-                           j + kAhead * kTile, j1);
+          issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, kRowsPerWave * (T - tb), ph_spread, a,
+                           j + kAhead * kTile, j1, ln);
       }
     }
   }
@@ -589,9 +618,14 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
   if (a.batch.num_rows <= 0) return hipSuccess;
   dim3 grid((unsigned)a.batch.num_rows, (unsigned)a.nsplit);
   if (lat_fmt == DSA_LATENT_FP8)
-    hipLaunchKernelGGL(sparse_mla_kernel<DSA_LATENT_FP8>, grid, dim3(kThreadsM), 0, s, a);
+    if (a.phys)
+      hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_FP8, true>), grid, dim3(kThreadsM), 0, s, a);
+    else
+      hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_FP8, false>), grid, dim3(kThreadsM), 0, s, a);
+  else if (a.phys)
+    hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_NVFP4, true>), grid, dim3(kThreadsM), 0, s, a);
   else
-    hipLaunchKernelGGL(sparse_mla_kernel<DSA_LATENT_NVFP4>, grid, dim3(kThreadsM), 0, s, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_NVFP4, false>), grid, dim3(kThreadsM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)a.batch.num_rows, 2 * kWavesM),
