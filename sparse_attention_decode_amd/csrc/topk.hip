@@ -145,8 +145,13 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a)
     for (int j = 0; j < kPerThread; ++j) v[j] = (j < avail) ? src[j] : 0.f;
   }
 
+  // the histogram row: every load in flight before the first is used
   const uint32_t* gh = a.hist_in + (int64_t)row * kBins;
-  for (int i = tid; i < kBins; i += kFilterThreads) hist[i] = gh[i];
+  uint32_t hv[kBins / kFilterThreads];
+#pragma unroll
+  for (int j = 0; j < kBins / kFilterThreads; ++j) hv[j] = gh[tid + kFilterThreads * j];
+#pragma unroll
+  for (int j = 0; j < kBins / kFilterThreads; ++j) hist[tid + kFilterThreads * j] = hv[j];
   __syncthreads();
   uint32_t rest;
   const uint32_t b1 = select_bin<kFilterThreads>(hist, kBins, (uint32_t)a.k, &rest, sc, wtot);
@@ -199,6 +204,11 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     return;
   }
   const int nsl = (n + kTopkSlice - 1) / kTopkSlice;
+  // The histogram row is loaded now (it is independent of everything below) and returned to
+  // zero for the next call.
+  uint32_t hv[kBins / kResolveThreads];
+#pragma unroll
+  for (int j = 0; j < kBins / kResolveThreads; ++j) hv[j] = hist_row[tid + kResolveThreads * j];
 
   // survivors per slice -> exclusive prefix
   {
@@ -226,20 +236,33 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     }
     return cand[lo * kTopkSlice + (int)(e - sh.pre[lo])];
   };
-  if (in_lds) {
-    for (uint32_t e = tid; e < M; e += kResolveThreads) {
-      const uint2 kv = cand_at(e);
-      sh.key[e] = kv.x;
-      sh.idx[e] = (int32_t)kv.y;
+  if (in_lds) {  // survivors in batches of 4 per thread, every load of a batch in flight at once
+    constexpr int kPer = 4;
+    for (uint32_t e0 = 0; e0 < M; e0 += kPer * kResolveThreads) {
+      uint2 kv[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t e = e0 + tid + kResolveThreads * j;
+        kv[j] = cand_at(e < M ? e : e0);  // e0 < M
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t e = e0 + tid + kResolveThreads * j;
+        if (e < M) {
+          sh.key[e] = kv[j].x;
+          sh.idx[e] = (int32_t)kv[j].y;
+        }
+      }
     }
   }
   auto key_of = [&](uint32_t e) -> uint32_t { return in_lds ? sh.key[e] : cand_at(e).x; };
   auto tok_of = [&](uint32_t e) -> int32_t { return in_lds ? sh.idx[e] : (int32_t)cand_at(e).y; };
 
   // level 1 from the histogram, which is then returned to zero for the next call
-  for (int i = tid; i < kBins; i += kResolveThreads) {
-    sh.hist[i] = hist_row[i];
-    hist_row[i] = 0;
+#pragma unroll
+  for (int j = 0; j < kBins / kResolveThreads; ++j) {
+    sh.hist[tid + kResolveThreads * j] = hv[j];
+    hist_row[tid + kResolveThreads * j] = 0;
   }
   __syncthreads();
   uint32_t need;
