@@ -169,11 +169,14 @@ __device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int 
 __device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid) {
   for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
     const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
+    // the four tokens' flags in one read; every row read unconditionally, then selected
+    const int4 ok = *reinterpret_cast<const int4*>(st.valid + 4 * tq);
+    const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
     uint32_t w[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = 4 * tq + u;
-      w[u] = st.valid[t] ? *reinterpret_cast<const uint32_t*>(st.raw + t * kRaw8 + 4 * db) : 0u;
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(st.raw + (4 * tq + u) * kRaw8 + 4 * db);
+      w[u] = okv[u] ? r : 0u;
     }
     // 4x4 byte transpose with byte permutes: out[i] = {w0.byte i, w1.byte i, w2.byte i, w3.byte i}
     const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
@@ -275,8 +278,10 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t raw3[kStages > 3 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw4[kStages > 4 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw5[kStages > 5 ? kRawBytes : 16];
-  __shared__ float tsc0[kSlots], tsc1[kSlots], tsc2[kSlots], tsc3[kSlots], tsc4[kSlots], tsc5[kSlots];
-  __shared__ int32_t valid0[kTile], valid1[kTile], valid2[kTile], valid3[kTile], valid4[kTile],
+  __shared__ __attribute__((aligned(16))) float tsc0[kSlots], tsc1[kSlots], tsc2[kSlots],
+      tsc3[kSlots], tsc4[kSlots], tsc5[kSlots];
+  __shared__ __attribute__((aligned(16))) int32_t valid0[kTile], valid1[kTile], valid2[kTile],
+      valid3[kTile], valid4[kTile],
       valid5[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
@@ -406,26 +411,36 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) sfr[h2] += sx[wave ^ 1][h2][ln];
 
-      // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head
+      // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head.  The four tokens'
+      // flags and scales are read at once, unconditionally; stale LDS bits of slots without a
+      // token are selected away, never used.
       float x[2][4], ts[2][4];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int t0 = 16 * h2 + 4 * gl;
+        const int4 ok4 = *reinterpret_cast<const int4*>(cur.valid + t0);
+        const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
+        float scv[4] = {a.tensor_scale, a.tensor_scale, a.tensor_scale, a.tensor_scale};
+        if constexpr (G::kFp8) {
+          const float4 s4 = *reinterpret_cast<const float4*>(cur.tsc + t0);
+          scv[0] = s4.x; scv[1] = s4.y; scv[2] = s4.z; scv[3] = s4.w;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = 16 * h2 + 4 * gl + i;
-          const bool ok = cur.valid[t];
-          // stale LDS bits of slots without a token are never used
-          const float scl = ok ? (G::kFp8 ? cur.tsc[t] : a.tensor_scale) : 0.f;
+          const bool ok = okv[i] != 0;
+          const float scl = ok ? scv[i] : 0.f;
           ts[h2][i] = scl;
           const float v = ok ? sfr[h2][i] * scl * qk_scale : -INFINITY;
           x[h2][i] = v;
           tmax = fmaxf(tmax, v);
         }
+      }
       tmax = xor32_max(xor16_max(tmax));
       // Lazy rescaling: the running max only moves when a logit exceeds it by more than 2^4, so
       // probabilities stay <= 16 and O is rarely rescaled.  The fp16 probability times the token
       // scale must stay finite: token (or tensor) scales below 4096.
+      const float m_old = m_run;
       const float m_new = (tmax > m_run + kLazyMax) ? tmax : m_run;
       const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
       float psum = 0.f;
@@ -448,7 +463,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       l_run = l_run * alpha + psum;
       m_run = m_new;
       const v8h pfrag = __builtin_bit_cast(v8h, uint4{pb[0], pb[1], pb[2], pb[3]});
-      if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f))) {  // wave-uniform, rarely taken
+      // wave-uniform, rarely taken; never while the running max is still -inf (O is all zeros)
+      if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f && m_old != -INFINITY))) {
 #pragma unroll
         for (int mt = 0; mt < kDvHalf / 16; ++mt) o[mt] *= alpha;
       }
