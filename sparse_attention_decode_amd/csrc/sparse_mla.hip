@@ -442,7 +442,10 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // scale must stay finite: token (or tensor) scales below 4096.
       const float m_old = m_run;
       const float m_new = (tmax > m_run + kLazyMax) ? tmax : m_run;
-      const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+      // v_exp_f32 directly (exp2(-inf) = 0; results below the fp32 normal range flush to zero,
+      // negligible next to the token that set the running max, whose probability is 1)
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float mref = (m_new == -INFINITY) ? 0.f : m_new;  // all logits -inf: p = 0, not NaN
       float psum = 0.f;
       uint32_t pb[4];
 #pragma unroll
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (x[h2][i] == -INFINITY) ? 0.f : exp2f(x[h2][i] - m_new);
+          const float p = __builtin_amdgcn_exp2f(x[h2][i] - mref);
           psum += p;
           pv[i] = p * ts[h2][i];  // the token scale of c_j multiplies its value row
         }
