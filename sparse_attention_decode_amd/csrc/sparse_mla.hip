@@ -27,10 +27,11 @@
 //         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
 //         The two partial S^T of a wave pair are added through LDS (both waves then hold the
 //         same bits, so their softmax statistics agree exactly).
-//   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  V^T comes from a dim-major copy of the
-//         value dims (FP8 bytes, or fp16 for NVFP4); P^T is S^T's softmax, already in B-operand
-//         position: the K order of this contraction is permuted so that lane group g holds
-//         tokens {4g..4g+3, 16+4g..16+4g+3}, and the dim-major tile stores tokens in that order.
+//   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  V^T comes from a dim-major fp16 copy of the
+//         value dims, converted once per tile for all head groups; P^T is S^T's softmax, already
+//         in B-operand position: the K order of this contraction is permuted so that lane group g
+//         holds tokens {4g..4g+3, 16+4g..16+4g+3}, and the dim-major tile stores tokens in that
+//         order.
 // Per-token scales stay out of the MFMA operands (they multiply the logits and the
 // probabilities), so every operand is an exact conversion of the stored codes.  fp16 for P keeps
 // its rounding well inside the output tolerance.  Softmax is online, in base 2.  With S^T and
@@ -70,17 +71,16 @@ constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabil
 
 // FP8 latents
 constexpr int kRaw8 = 592;   // raw row bytes: 576 codes + pad (148 dwords: b128 reads conflict-free)
-constexpr int kVt8 = 40;     // dim-major row bytes: 32 tokens + pad (10 dwords)
 // NVFP4 latents
 constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
 constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords)
-constexpr int kVt4 = 80;     // fp16 dim-major row bytes: 64 + pad (20 dwords)
+constexpr int kVt4 = 80;     // fp16 dim-major row bytes (both formats): 64 + pad (20 dwords)
 
 template <int LFMT>
 struct Geo {
   static constexpr bool kFp8 = LFMT == DSA_LATENT_FP8;
   static constexpr int kRaw = kFp8 ? kRaw8 : kRaw4;
-  static constexpr int kVt = kFp8 ? kVt8 : kVt4;
+  static constexpr int kVt = kVt4;
   static constexpr int kCtBytes = kFp8 ? 16 : kTile * kCt4;  // decoded tile (NVFP4 only)
 };
 
@@ -164,32 +164,35 @@ __device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int 
   }
 }
 
-// FP8: dim-major copy of the value dims of a stage (bytes, transposed in 4x4 blocks); tokens that
-// are not selected get zeros so that their (zero) probabilities never meet stale data.
+// FP8: dim-major fp16 copy of the value dims of a stage, converted once per tile for all head
+// groups (fp8 -> fp16 is exact).  A thread takes a block of 4 dims x 4 tokens: two conversions
+// per token give its four values as two half-word pairs, and half-word permutes transpose them
+// into four dim rows of 4 tokens.  Tokens that are not selected get zeros, so their (zero)
+// probabilities never meet stale data.
 __device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid) {
   for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
     const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
     // the four tokens' flags in one read; every row read unconditionally, then selected
     const int4 ok = *reinterpret_cast<const int4*>(st.valid + 4 * tq);
     const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
-    uint32_t w[4];
+    uint32_t lo[4], hi[4];  // token u: fp16 of dims (4db, 4db+1) and of (4db+2, 4db+3)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t r = *reinterpret_cast<const uint32_t*>(st.raw + (4 * tq + u) * kRaw8 + 4 * db);
-      w[u] = okv[u] ? r : 0u;
+      uint32_t r = *reinterpret_cast<const uint32_t*>(st.raw + (4 * tq + u) * kRaw8 + 4 * db);
+      r = okv[u] ? r : 0u;
+      lo[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, false));
+      hi[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, true));
     }
-    // 4x4 byte transpose with byte permutes: out[i] = {w0.byte i, w1.byte i, w2.byte i, w3.byte i}
-    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
-    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
-    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
-    const uint32_t v[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                           __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
-                           __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
-                           __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint32_t*>(vt + (4 * db + i) * kVt8 + vt_pos(4 * tq)) = v[i];
+    // dim row 4db+i: tokens 0..3 of the quad, K slots vt_pos(4 tq) .. +3
+    uint8_t* row = vt + 4 * db * kVt4 + 2 * vt_pos(4 * tq);
+    *reinterpret_cast<uint2*>(row) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u),
+                                           __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
+    *reinterpret_cast<uint2*>(row + kVt4) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
+                                                  __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)};
+    *reinterpret_cast<uint2*>(row + 2 * kVt4) = uint2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u),
+                                                      __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
+    *reinterpret_cast<uint2*>(row + 3 * kVt4) = uint2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
+                                                      __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)};
   }
 }
 
@@ -235,14 +238,6 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(v8bf, r);
 }
 
-__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
-  const uint4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
-  return __builtin_bit_cast(v8h, r);
-}
-
 // K step i of contraction half dh: lane group g holds dims [288dh + 32i + 8g, +8).  The nine steps
 // of a half cover its 288 dims once; A and B operands use the same dims.
 constexpr int kHalfDims = DSA_MLA_DQK / 2;
@@ -258,15 +253,9 @@ __device__ __forceinline__ v8bf qk_operand(const Stage& st, const uint8_t* ct, i
   }
 }
 
-// Dim-major value tile as the A operand of PV: dim row d, lane group g (8 K slots).
-template <int LFMT>
+// Dim-major fp16 value tile as the A operand of PV: dim row d, lane group g (8 K slots).
 __device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int g) {
-  if constexpr (LFMT == DSA_LATENT_FP8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(vt + d * kVt8 + 8 * g);
-    return fp8x8_to_f16(v.x, v.y);
-  } else {
-    return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 16 * g));
-  }
+  return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 16 * g));
 }
 
 // PHYS: the select's physical pool rows are given (else selected indices + block table).
@@ -475,7 +464,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // O^T (dims x heads) += V^T P^T; A operand lane: dim 256dh + 16mt + c, K slots 8g .. 8g+7
 #pragma unroll
       for (int mt = 0; mt < kDvHalf / 16; ++mt)
-        o[mt] = mfma_f16(pv_operand<LFMT>(vt, kDvHalf * dh + 16 * mt + cl, gl), pfrag, o[mt]);
+        o[mt] = mfma_f16(pv_operand(vt, kDvHalf * dh + 16 * mt + cl, gl), pfrag, o[mt]);
 
       // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
       // first barrier, so no one reads it any more).  Issued last: a wave that finds the gather
