@@ -541,6 +541,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 // (mt8, lane) takes accumulator block mt = 8 * blockIdx.y % 2 + mt8 of the attention wave
 // blockIdx.y / 2, i.e. head 16 * (wave / 2) + lane % 16, dims 256 * (wave % 2) + 16 mt + 4 (lane / 16)
 // + 0..3.  Partial loads are 8 contiguous bytes per thread (4 KB per workgroup and split).
+// G: splits per group (4, 8 or 16), the smallest that covers nsplit when it can.
+template <int G>
 __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   const int row = blockIdx.x;
   const int wave = blockIdx.y >> 1;
@@ -553,41 +555,42 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
                        ((int64_t)row * a.nsplit * kWavesM + wave) * (kDvHalf / 16) * kWave +
                        mt * kWave + lane;
   const int64_t pstride = (int64_t)kWavesM * (kDvHalf / 16) * kWave;  // one split
-  // splits in groups of 8 with every load of a group issued before it is used
-  constexpr int G = 8;
-  float M = -INFINITY;
+  // One pass over groups of G splits: every load of a group (log-sum-exp, exponent and partial)
+  // is in flight before any is used, and a running maximum rescales what earlier groups added,
+  // so up to G splits take one memory round trip.
+  float M = -INFINITY, L = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.nsplit; s0 += G) {
     float ls[G];
+    int ex[G];
+    uint2 v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int sp = min(s0 + u, a.nsplit - 1);  // past the end: a repeat, weighted 0 below
+      ls[u] = a.part_lse[hbase + (int64_t)sp * DSA_MLA_HEADS];
+      ex[u] = a.part_exp[hbase + (int64_t)sp * DSA_MLA_HEADS];
+      v[u] = pbase[(int64_t)sp * pstride];
+    }
+    float gm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      ls[u] = s0 + u < a.nsplit ? a.part_lse[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
+      if (s0 + u < a.nsplit) gm = fmaxf(gm, ls[u]);
+    const float m_new = fmaxf(M, gm);
+    if (m_new == -INFINITY) continue;  // nothing attended so far
+    const float r = exp2f(M - m_new);  // M = -inf: 0 (L and acc are 0 then)
+    L *= r;
 #pragma unroll
-    for (int u = 0; u < G; ++u) M = fmaxf(M, ls[u]);
-  }
-  float L = 0.f;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < a.nsplit; s0 += G) {
-      float ls[G];
-      int ex[G];
-      uint2 v[G];
+    for (int i = 0; i < 4; ++i) acc[i] *= r;
+    M = m_new;
 #pragma unroll
-      for (int u = 0; u < G; ++u) {
-        const bool in = s0 + u < a.nsplit;
-        ls[u] = in ? a.part_lse[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : -INFINITY;
-        ex[u] = in ? a.part_exp[hbase + (int64_t)(s0 + u) * DSA_MLA_HEADS] : 0;
-        v[u] = in ? pbase[(int64_t)(s0 + u) * pstride] : uint2{0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < G; ++u) {
-        const float wgt = (ls[u] == -INFINITY) ? 0.f : exp2f(ls[u] - M);
-        L += wgt;
-        const float w2 = ldexpf(wgt, -ex[u]);
-        acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
-        acc[1] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16));
-        acc[2] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu));
-        acc[3] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16));
-      }
+    for (int u = 0; u < G; ++u) {
+      const float wgt = (s0 + u < a.nsplit && ls[u] != -INFINITY) ? exp2f(ls[u] - M) : 0.f;
+      L += wgt;
+      const float w2 = ldexpf(wgt, -ex[u]);
+      acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
+      acc[1] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16));
+      acc[2] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu));
+      acc[3] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16));
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -636,8 +639,13 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
     hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_NVFP4, false>), grid, dim3(kThreadsM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)a.batch.num_rows, 2 * kWavesM),
-                     dim3(512), 0, s, a);
+  const dim3 cgrid((unsigned)a.batch.num_rows, 2 * kWavesM);
+  if (a.nsplit <= 4)
+    hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
+  else if (a.nsplit <= 8)
+    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
