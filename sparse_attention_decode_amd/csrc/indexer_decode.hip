@@ -27,7 +27,7 @@ constexpr int kThreads = 256;         // 4 waves
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
 constexpr int kPrefillRows = 16;      // rows per workgroup tile on the prefill path
 constexpr int kMaxPagesPerWave = 64;  // one block-table entry per lane
-constexpr int kMaxPagesSmallR = 16;   // one or two rows: the whole run's scores in registers
+constexpr int kMaxPagesSmallR = 8;    // one or two rows: the whole run's scores in registers
 
 // Operand fragments of one 16-token tile.
 struct KeyFrag {
@@ -335,15 +335,18 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   IndexerArgs a = a0;
   a.tiles_per_seq = 1;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
-  // Workgroups: about 768 (three per CU) for one or two rows, 2048 for more, from the longest
-  // sequence; pages per wave a multiple of 4, at most 16 (one or two rows: the run's scores stay
-  // in registers, and ragged batches keep enough workgroups) or 64.
+  // Workgroups, from the longest sequence: about 1024 for one or two rows (4 to 8 pages per
+  // wave; with three workgroups resident per CU that is about 1.3 rounds, so the score stores of
+  // the first round overlap the key reads of the second: measured faster than one round of 688
+  // or 2048 workgroups), about 2048 for more rows (pages per wave a multiple of the 4-page store
+  // group, at most 64).
   constexpr int kWaves = kThreads / kWave;
-  const int64_t target = rows_per_seq <= 2 ? 768 : 2048;
-  const int64_t cap = rows_per_seq <= 2 ? kMaxPagesSmallR : kMaxPagesPerWave;
+  const bool small = rows_per_seq <= 2;
+  const int64_t target = small ? 1024 : 2048;
+  const int64_t cap = small ? kMaxPagesSmallR : kMaxPagesPerWave;
   const int64_t want = (nblk * a.batch.num_seqs + target - 1) / target;
   int64_t ppw = (want + kWaves - 1) / kWaves;
-  ppw = (ppw + 3) / 4 * 4;
+  if (!small) ppw = (ppw + 3) / 4 * 4;
   if (ppw < 4) ppw = 4;
   if (ppw > cap) ppw = cap;
   a.pages_per_wave = (int32_t)ppw;
