@@ -8,7 +8,7 @@ consecutive steps rotate over independent batches (separate pools) so the 277 MB
 read from HBM rather than from the 256 MB memory-side cache.  Inputs are resident in HBM before
 the timed region.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4] [--no-graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..5] [--no-graph]
 """
 from __future__ import annotations
 
@@ -161,7 +161,7 @@ def main():
     import synth.device
 
     cfg = args.config
-    reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4}[cfg]
+    reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2}[cfg]
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
     wls, devs, layers = [], [], []
@@ -237,7 +237,7 @@ def main():
     layer_gbps = total_b / (ms_step * 1e-3) / 1e9
     idx_gbps = idx_b / (idx_ms * 1e-3) / 1e9
     flops = indexer_flops(wl)
-    prefill = cfg == 3
+    prefill = cfg in (3, 5)
     if prefill:
         roof = {"bound": "mfma", "achieved": flops / (idx_ms * 1e-3) / 1e12,
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}

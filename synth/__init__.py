@@ -259,9 +259,10 @@ def seq_tensors(w: Workload, b: int, ntok: int | None = None):
 # ----------------------------------------------------------------------------- named shapes
 
 def decode_config(i: int, seed: int | None = None, replica: int = 0) -> Workload:
-    """The five layer shapes this project measures (decode 8K, batched decode 16 x 128K,
-    speculative decode 16 x (1+5) at 1M, chunked prefill 8192 on 339,968, mixed-length
-    64 x log-uniform[4K, 256K] with MXFP4 keys and NVFP4 latents)."""
+    """The layer shapes this project measures: 0 decode 8K, 1 batched decode 16 x 128K,
+    2 speculative decode 16 x (1+5) at 1M, 3 chunked prefill 8192 on 339,968, 4 mixed-length
+    64 x log-uniform[4K, 256K] with MXFP4 keys and NVFP4 latents, 5 short-append prefill
+    2048 on 150,000."""
     seed = (1000 + i + 7919 * replica) if seed is None else seed
     if i == 0:
         return Workload("decode-1x8K", seed, [8192], [0], [8191])
@@ -276,6 +277,10 @@ def decode_config(i: int, seed: int | None = None, replica: int = 0) -> Workload
     if i == 3:
         P, T = 339968, 8192
         return Workload("prefill-8192-on-339968", seed, [P + T], [0] * T,
+                        [P + t for t in range(T)])
+    if i == 5:
+        P, T = 150000, 2048
+        return Workload("prefill-2048-on-150000", seed, [P + T], [0] * T,
                         [P + t for t in range(T)])
     if i == 4:
         g = np.random.Generator(np.random.PCG64(seed + 1))

@@ -1,4 +1,4 @@
-"""Parity of the HIP path with the oracle at the full sizes of the five measured workloads, in the
+"""Parity of the HIP path with the oracle at the full sizes of the six measured workloads, in the
 launch configuration the benchmark times (scorer with its fused histogram, select emitting
 physical rows, attention reading them; prefill variants for the 8,192-row chunk).  The whole
 batch runs on the GPU; sampled rows are recomputed by the oracle one by one and compared element
@@ -66,6 +66,15 @@ def test_full_prefill_8192_on_339968():
     assert layer.prefill
     _check_sampled(wl, layer, _sample_rows(wl, [0, 4095, 8191]))
     # every row has more than 2048 visible tokens: a full selection
+    assert int(layer.count.min().item()) == wl.k
+
+
+def test_full_prefill_2048_on_150000():
+    # the short-append prefill: 2,048 rows after a 150,000-token prefix
+    wl = synth.decode_config(5)
+    layer, _, _ = run_gpu(wl)
+    assert layer.prefill
+    _check_sampled(wl, layer, _sample_rows(wl, [0, 1023, 2047]))
     assert int(layer.count.min().item()) == wl.k
 
 
