@@ -113,7 +113,15 @@ typedef struct dsa_batch {
   const int32_t* block_table;   /* [num_seqs * max_blocks_per_seq] pool row ids */
   const int32_t* seq_row_start; /* [num_seqs + 1] rows of sequence b: [start[b], start[b+1]) */
   const int32_t* row_pos;       /* [num_rows] */
+  uint32_t flags;               /* host: 0 or DSA_BATCH_INVARIANT (any other bit: INVALID_ARG) */
 } dsa_batch;
+
+/* dsa_batch.flags: the attention splits each row's selected set into fixed 128-token parts, in
+ * sparse_mla_decode and sparse_mla_prefill alike, so a row's outputs are bit-identical whichever
+ * rows share its batch and whichever of the two runs it (the page's batch-invariant kernels).
+ * Without it the split count follows the row count (faster; outputs then agree within rounding
+ * between batches of different row counts).  Scores and the select are batch-invariant always. */
+#define DSA_BATCH_INVARIANT 1u
 
 /* Fill *out (host) with the pool layout for the given formats (block_size must be 64).
  * Returns INVALID_ARG for a null pointer or bad value, UNSUPPORTED for another block size. */
@@ -164,8 +172,9 @@ DSA_API dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, con
                             int32_t* count, int32_t* phys, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sparse_mla_decode needs for num_rows rows and top-k k. */
-DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k);
+/* Workspace bytes sparse_mla_decode needs for num_rows rows and top-k k with dsa_batch.flags
+ * `flags` (sparse_mla_prefill needs none unless flags has DSA_BATCH_INVARIANT: then this size). */
+DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k, uint32_t flags);
 
 /*
  * Step 3 — exact MLA attention over the selected latents (page: every query head attends

@@ -43,7 +43,11 @@ class Batch(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("max_rows_per_seq", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("max_context", ctypes.c_int64), ("block_table", ctypes.c_void_p),
-                ("seq_row_start", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
+                ("seq_row_start", ctypes.c_void_p), ("row_pos", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
+
+
+BATCH_INVARIANT = 1  # dsa_batch.flags: attention split count from k alone (see include/dsa.h)
 
 
 _lib = None
@@ -68,7 +72,7 @@ def lib():
         L.dsa_topk.argtypes = [ctypes.POINTER(KVLayout), ctypes.POINTER(Batch), vp, i64, vp, i32,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sparse_mla_workspace_bytes.restype = ctypes.c_size_t
-        L.sparse_mla_workspace_bytes.argtypes = [i32, i32]
+        L.sparse_mla_workspace_bytes.argtypes = [i32, i32, ctypes.c_uint32]
         for fn in ("sparse_mla_decode", "sparse_mla_prefill"):
             f = getattr(L, fn)
             f.restype = i32
@@ -109,7 +113,7 @@ class DeviceBatch:
     """A dsa_batch plus the device tensors it points at (kept alive here)."""
 
     def __init__(self, block_table, seq_row_start, row_pos, max_rows_per_seq: int,
-                 max_context: int):
+                 max_context: int, flags: int = 0):
         self.block_table, self.seq_row_start, self.row_pos = block_table, seq_row_start, row_pos
         b = Batch()
         b.num_seqs = seq_row_start.numel() - 1
@@ -120,6 +124,7 @@ class DeviceBatch:
         b.block_table = block_table.data_ptr()
         b.seq_row_start = seq_row_start.data_ptr()
         b.row_pos = row_pos.data_ptr()
+        b.flags = int(flags)
         self.c = b
 
     @property
@@ -146,8 +151,8 @@ def dsa_topk(kv: KVLayout | None, batch: DeviceBatch, scores, hist, k: int, idx,
                           _ptr(phys), _ptr(workspace), ws_bytes, _stream(stream)), "dsa_topk")
 
 
-def sparse_mla_workspace_bytes(num_rows: int, k: int) -> int:
-    return int(lib().sparse_mla_workspace_bytes(num_rows, k))
+def sparse_mla_workspace_bytes(num_rows: int, k: int, flags: int = 0) -> int:
+    return int(lib().sparse_mla_workspace_bytes(num_rows, k, flags))
 
 
 def _mla(fn: str, kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, workspace, stream):

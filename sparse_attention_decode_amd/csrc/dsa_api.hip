@@ -63,6 +63,7 @@ dsa_status check_batch(const dsa_batch* b) {
     return fail(DSA_ERR_INVALID_ARG, "max_blocks_per_seq * 64 < max_context");
   if (!b->block_table || !b->seq_row_start || !b->row_pos)
     return fail(DSA_ERR_INVALID_ARG, "block_table, seq_row_start and row_pos must be non-NULL");
+  if (b->flags & ~DSA_BATCH_INVARIANT) return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
   return DSA_OK;
 }
 
@@ -116,14 +117,15 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.tensor_scale = kv->latent_format == DSA_LATENT_NVFP4 ? kv->latent_tensor_scale : 1.f;
   a.out = out;
   a.lse = lse;
-  a.nsplit = prefill ? 1 : dsa::mla_num_splits(batch->num_rows, k);
+  const bool invariant = (batch->flags & DSA_BATCH_INVARIANT) != 0;
+  a.nsplit = (prefill && !invariant) ? 1 : dsa::mla_num_splits(batch->num_rows, k, invariant);
   a.tokens_per_split = (int32_t)align_up((k + a.nsplit - 1) / a.nsplit, 32);
   a.nsplit = (k + a.tokens_per_split - 1) / a.tokens_per_split;
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.part_exp = nullptr;
   if (a.nsplit > 1) {
-    const size_t need = dsa::mla_workspace_bytes(batch->num_rows, k);
+    const size_t need = dsa::mla_workspace_bytes(batch->num_rows, k, invariant);
     if (!workspace || workspace_bytes < need)
       return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -265,9 +267,10 @@ dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float
                     "topk launch");
 }
 
-size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k) {
+size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k, uint32_t flags) {
   if (num_rows <= 0 || k < 1) return 0;
-  return dsa::mla_workspace_bytes(num_rows, k > DSA_MAX_TOPK ? DSA_MAX_TOPK : k);
+  return dsa::mla_workspace_bytes(num_rows, k > DSA_MAX_TOPK ? DSA_MAX_TOPK : k,
+                                  (flags & DSA_BATCH_INVARIANT) != 0);
 }
 
 dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,

@@ -75,8 +75,8 @@ struct MlaArgs {
   int32_t nsplit;
   int32_t tokens_per_split;
 };
-int mla_num_splits(int32_t num_rows, int32_t k);
-size_t mla_workspace_bytes(int32_t num_rows, int32_t k);
+int mla_num_splits(int32_t num_rows, int32_t k, bool invariant);
+size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant);
 hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s);
 
 }  // namespace dsa

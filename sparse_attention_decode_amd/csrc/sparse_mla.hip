@@ -611,7 +611,10 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
 #endif
-int mla_num_splits(int32_t num_rows, int32_t k) {
+// Splits of each row's selected set: enough workgroups to fill the chip (about 256), or, for a
+// batch-invariant call, fixed 128-token parts (a function of k alone).
+int mla_num_splits(int32_t num_rows, int32_t k, bool invariant) {
+  if (invariant) return (k + 4 * kTile - 1) / (4 * kTile);
   const int tiles = (k + kTile - 1) / kTile;
   int want = (DSA_MLA_TARGET_WGS + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
   if (want > tiles) want = tiles;
@@ -619,8 +622,8 @@ int mla_num_splits(int32_t num_rows, int32_t k) {
   return want;
 }
 
-size_t mla_workspace_bytes(int32_t num_rows, int32_t k) {
-  const int ns = mla_num_splits(num_rows, k);
+size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant) {
+  const int ns = mla_num_splits(num_rows, k, invariant);
   if (ns <= 1) return 0;
   return (size_t)num_rows * ns * DSA_MLA_HEADS * (DSA_MLA_DV * sizeof(uint16_t) + 2 * sizeof(float));
 }

@@ -35,7 +35,9 @@ class DSALayer:
         self.lse = torch.empty((R, L.MLA_HEADS), dtype=torch.float32, device=device)
         tb = L.dsa_topk_workspace_bytes(R, batch.c.max_context)
         self.topk_ws = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=device)
-        nbytes = 0 if prefill else L.sparse_mla_workspace_bytes(R, k)
+        flags = batch.c.flags
+        nbytes = 0 if (prefill and not flags & L.BATCH_INVARIANT) else \
+            L.sparse_mla_workspace_bytes(R, k, flags)
         self.workspace = (torch.empty((max(nbytes, 16) + 15) // 16 * 4, dtype=torch.float32,
                                       device=device) if nbytes else None)
 

@@ -13,13 +13,13 @@ import synth.device
 RTOL, ATOL = 2e-2, 2e-3  # bf16 outputs and fp32 log-sum-exp against the float64 oracle
 
 
-def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, phys=True):
+def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, phys=True, flags=0):
     kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
     d = synth.device.stage(wl, kv.as_dict())
     if zero_qidx:
         d["q_idx"].zero_()
     batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
-                            d["max_rows_per_seq"], d["max_context"])
+                            d["max_rows_per_seq"], d["max_context"], flags)
     if prefill is None:
         prefill = d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ
     layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale, prefill=prefill, use_hist=use_hist)

@@ -102,7 +102,7 @@ def test_entry_points_validate_before_launch():
                         need - 1, None) == L.DSA_ERR_WORKSPACE
     # decode MLA with several splits needs its workspace
     b3 = _fake_batch(num_rows=1)
-    need = lib.sparse_mla_workspace_bytes(1, 2048)
+    need = lib.sparse_mla_workspace_bytes(1, 2048, 0)
     assert need > 0
     assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, None, 2048, 0.1,
                                  p, None, None, 0, None) == L.DSA_ERR_WORKSPACE
@@ -114,6 +114,27 @@ def test_entry_points_validate_before_launch():
     assert lib.dsa_indexer_scores(ctypes.byref(kv4), pool, ctypes.byref(b4), p, p, p, 128, None,
                                   None) == L.DSA_ERR_UNSUPPORTED
     assert lib.dsa_status_string(L.DSA_ERR_WORKSPACE) == b"DSA_ERR_WORKSPACE"
+
+
+def test_batch_flags():
+    # Unknown flag bits are rejected before any launch; the batch-invariant split count depends
+    # on k alone, so its workspace is rows x 16 splits for k = 2048, also on the prefill path.
+    lib = L.lib()
+    kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    pool = ctypes.c_void_p(0x100000)
+    p = ctypes.c_void_p(0x2000)
+    bad = _fake_batch(flags=2)
+    assert lib.dsa_indexer_scores(ctypes.byref(kv), pool, ctypes.byref(bad), p, p, p, 128, None,
+                                  None) == L.DSA_ERR_INVALID_ARG
+    assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(bad), p, p, p, 2048, 0.1,
+                                 p, None, p, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
+    per_slot = sad.MLA_DV * 2 + 8
+    assert lib.sparse_mla_workspace_bytes(8192, 2048, 0) == 0
+    assert lib.sparse_mla_workspace_bytes(8192, 2048, sad.BATCH_INVARIANT) == 8192 * 16 * 96 * per_slot
+    assert lib.sparse_mla_workspace_bytes(3, 2048, sad.BATCH_INVARIANT) == 3 * 16 * 96 * per_slot
+    inv = _fake_batch(flags=sad.BATCH_INVARIANT, num_rows=64, max_rows_per_seq=64)
+    assert lib.sparse_mla_prefill(ctypes.byref(kv), pool, ctypes.byref(inv), p, p, p, 2048, 0.1,
+                                  p, None, None, 0, None) == L.DSA_ERR_WORKSPACE
 
 
 def test_empty_batch_is_a_no_op():
@@ -128,7 +149,7 @@ def test_empty_batch_is_a_no_op():
     assert lib.dsa_topk_workspace_bytes(0, 100) == 0
     assert lib.dsa_topk(ctypes.byref(kv), ctypes.byref(b), p, 128, p, 16, p, p, p, None, 0,
                         None) == L.DSA_OK
-    assert lib.sparse_mla_workspace_bytes(0, 2048) == 0
+    assert lib.sparse_mla_workspace_bytes(0, 2048, 0) == 0
     for fn in (lib.sparse_mla_decode, lib.sparse_mla_prefill):
         assert fn(ctypes.byref(kv), pool, ctypes.byref(b), p, p, p, 2048, 0.1, p, None, None, 0,
                   None) == L.DSA_OK

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_attention_decode_amd as sad
 import synth
 from gpu_harness import ATOL, RTOL, check_rows, oracle_seq, run_gpu
 
@@ -60,3 +61,21 @@ def test_rows_independent_of_batch():
     # the rows of the smaller batch still match the oracle (one row per sequence)
     for r in where(alone):
         check_rows(alone, la, oracle_seq(alone, r, rows=[r]), [r])
+
+
+def test_batch_invariant_flag():
+    inv = sad.BATCH_INVARIANT
+    base = _batch("invariance-base", [1, 2, 4, 6, 7, 8])
+    alone = _batch("invariance-alone", [2, 4, 1])
+    shared = [1, 2, 4]
+    where = lambda wl: [int(np.nonzero(wl.seq_id == i)[0][0]) for i in shared]
+    runs = []
+    for wl, prefill in ((base, False), (alone, False), (alone, True)):
+        layer, _, _ = run_gpu(wl, flags=inv, prefill=prefill)
+        assert layer.prefill == prefill
+        runs.append(_results(layer, where(wl)))
+        del layer
+        torch.cuda.empty_cache()
+    for other, what in ((runs[1], "a smaller batch"), (runs[2], "the prefill entry point")):
+        for a, b, name in zip(runs[0][:4], other[:4], ("idx", "count", "output bits", "lse")):
+            assert np.array_equal(a, b), f"{name} differ on {what} with DSA_BATCH_INVARIANT"
