@@ -8,7 +8,9 @@ Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" (§Sparse Attention in K
 cache for three kinds of state; §AMD / Quantization: Native MXFP4 indexer).  The indexer rule is
 DeepSeek-V3.2's lightning indexer, to which the pages defer:
     score[s] = sum_h w[h] * ReLU(scale_s * q[h] . k[s]).
-Parity pins: see tests/test_oracle.py and tests/test_codecs.py.
+The quantisers (the step before the path, §Low-latency decode: a fused DSA decode path) quantise
+the new token's index key and latent and the indexer query.
+Parity pins: see tests/test_oracle.py, tests/test_codecs.py and tests/test_oracle_quant.py.
 """
 from __future__ import annotations
 
@@ -64,6 +66,17 @@ def lib():
         L.orc_dsa_rows.restype = i64
         L.orc_dsa_rows.argtypes = [i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp,
                                    ctypes.c_float, i32, d, vp, vp, vp, vp, vp]
+        L.orc_quant_e4m3.restype = ctypes.c_uint8
+        L.orc_quant_e4m3.argtypes = [ctypes.c_float]
+        L.orc_quant_e2m1.restype = ctypes.c_uint8
+        L.orc_quant_e2m1.argtypes = [ctypes.c_float]
+        for f in (L.orc_quant_fp8_token, L.orc_quant_mxfp4_key, L.orc_quant_nvfp4_latent,
+                  L.orc_quantize_query):
+            f.restype = None
+        L.orc_quant_fp8_token.argtypes = [i32, vp, vp, vp]
+        L.orc_quant_mxfp4_key.argtypes = [i32, vp, vp, vp]
+        L.orc_quant_nvfp4_latent.argtypes = [i32, vp, ctypes.c_float, vp, vp]
+        L.orc_quantize_query.argtypes = [i32, i32, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -210,3 +223,58 @@ def workload_rows(wl, b: int, rows=None, ntok=None, want_scores=False):
         qm[i] = synth.qmla(wl.seed, int(wl.row_id[r]), 1)[0]
     return dsa_rows(wl.ikey_fmt, wl.lat_fmt, wl.row_pos[rows], qi, hw, qm, keys, ks, lat, ls,
                     wl.lat_tensor_scale, wl.k, wl.softmax_scale, want_scores)
+
+
+# ----------------------------------------------------------------------------- quantisers
+# (the step before the path: writing the new token into its paged row, quantising the query)
+
+def quant_e4m3(x) -> np.ndarray:
+    """e4m3 codes of fp32 values: nearest, ties to even, saturating at 448."""
+    a = np.asarray(x, np.float32)
+    L = lib()
+    return np.array([L.orc_quant_e4m3(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+
+def quant_e2m1(x) -> np.ndarray:
+    """e2m1 nibbles of fp32 values: nearest, ties to even, saturating at 6."""
+    a = np.asarray(x, np.float32)
+    L = lib()
+    return np.array([L.orc_quant_e2m1(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+
+def quant_fp8_token(x_bf16):
+    """[D] bf16 bits -> (codes [D] e4m3, scale f32)."""
+    x = _c(x_bf16, np.uint16)
+    codes = np.empty(x.size, np.uint8)
+    s = np.empty(1, np.float32)
+    lib().orc_quant_fp8_token(x.size, _p(x), _p(codes), _p(s))
+    return codes, float(s[0])
+
+
+def quant_mxfp4_key(x_bf16):
+    """[D] bf16 bits -> (packed e2m1 [D/2], e8m0 scales [D/32])."""
+    x = _c(x_bf16, np.uint16)
+    packed = np.empty(x.size // 2, np.uint8)
+    sc = np.empty(x.size // 32, np.uint8)
+    lib().orc_quant_mxfp4_key(x.size, _p(x), _p(packed), _p(sc))
+    return packed, sc
+
+
+def quant_nvfp4_latent(x_bf16, tensor_scale: float):
+    """[D] bf16 bits -> (packed e2m1 [D/2], e4m3 block scales [D/16])."""
+    x = _c(x_bf16, np.uint16)
+    packed = np.empty(x.size // 2, np.uint8)
+    sc = np.empty(x.size // 16, np.uint8)
+    lib().orc_quant_nvfp4_latent(x.size, _p(x), float(tensor_scale), _p(packed), _p(sc))
+    return packed, sc
+
+
+def quantize_query(q_bf16, w):
+    """q [H,D] bf16 bits, w [H] f32 -> (codes [H,D] e4m3, w' [H] f32)."""
+    q = _c(q_bf16, np.uint16)
+    w = _c(w, np.float32)
+    H, D = q.shape
+    codes = np.empty((H, D), np.uint8)
+    wout = np.empty(H, np.float32)
+    lib().orc_quantize_query(H, D, _p(q), _p(w), _p(codes), _p(wout))
+    return codes, wout

@@ -10,6 +10,9 @@
  *   [K31] "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" (wpnews.pro), sections
  *         "Sparse Attention in K3.1 Pro", "KV cache footprint", "A KV cache for three kinds of
  *         state", "AMD / Quantization: Native MXFP4 indexer".
+ *   [K31] also, section "Low-latency decode: a fused DSA decode path", for the step before the
+ *         path: the indexer query quantised with its head weights folded in, and the new token's
+ *         index key and latent written into the cache (the quantisers at the end of this file).
  *   The pages defer the indexer's scoring rule to DeepSeek-V3.2's lightning indexer; the rule
  *   used here is that indexer's: score = sum_h w[h] * ReLU(scale_s * q[h] . k[s]).
  *   Number formats follow their published definitions: OCP 8-bit Floating Point (E4M3),
@@ -25,7 +28,10 @@
  * head-permutation invariance; top-k against its defining order property and brute force on
  * tiny inputs; attention against float64 scaled-dot-product attention from torch when the
  * selected set is every visible token, against single-token / identical-latent / q = 0 closed
- * forms, and against permutation and causality invariants.
+ * forms, and against permutation and causality invariants; quantisers against an arithmetic
+ * round-half-even formulation on each format's grid, midpoints, saturation, exact round trips of
+ * representable tokens, the scale rules and error bounds of each format, and the query-scale fold
+ * through the scoring rule.
  */
 #include <math.h>
 #include <stdint.h>
@@ -287,4 +293,110 @@ int64_t orc_dsa_rows(int key_fmt, int lat_fmt, int nrows, const int64_t* row_pos
   free(sc32);
   free(c);
   return mism;
+}
+
+/* ------------------------------------------------------------------ quantisers (the step
+ * before the path: the new token's index key and latent written into its paged row, and the
+ * indexer query quantised with its scale folded into the head weight; [K31] "A KV cache for three
+ * kinds of state" for the formats, "Low-latency decode: a fused DSA decode path" for the step).
+ *
+ * Rounding is round-to-nearest, ties to the even code (mantissa LSB 0), found by exhaustive
+ * search over the finite codes of the format; a magnitude beyond the largest finite value takes
+ * the largest (saturation).  The sign bit is that of x (so -0 and negative values rounding to 0
+ * give the negative zero code).  Arithmetic on the way (amax, the division by the scale) is in
+ * fp32, as a kernel does it. */
+
+static uint8_t nearest_mag(double a, int ncodes, double (*dec)(uint8_t)) {
+  uint8_t best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c < ncodes; ++c) {
+    const double d = fabs(dec((uint8_t)c) - a);
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = (uint8_t)c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* e4m3 code of x: magnitudes 0x00..0x7E (0x7F is NaN). */
+uint8_t orc_quant_e4m3(float x) {
+  return (uint8_t)((signbit(x) ? 0x80 : 0) | nearest_mag(fabs((double)x), 0x7F, orc_e4m3));
+}
+
+/* e2m1 nibble of x: magnitudes 0..7. */
+uint8_t orc_quant_e2m1(float x) {
+  return (uint8_t)((signbit(x) ? 0x8 : 0) | nearest_mag(fabs((double)x), 8, orc_e2m1));
+}
+
+static float bf16f(uint16_t b) { return (float)orc_bf16(b); }
+
+static float amax_bf16(int n, const uint16_t* x) {
+  float m = 0.f;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, fabsf(bf16f(x[i])));
+  return m;
+}
+
+/* One token of D bf16 values as FP8 with a per-token scale: s = amax / 448 (1 when amax is 0),
+ * code_d = e4m3(x_d / s).  (FP8 index keys and FP8 latents.) */
+void orc_quant_fp8_token(int D, const uint16_t* x, uint8_t* codes, float* scale) {
+  const float amax = amax_bf16(D, x);
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int d = 0; d < D; ++d) codes[d] = orc_quant_e4m3(bf16f(x[d]) / s);
+  *scale = s;
+}
+
+/* One MXFP4 index key (OCP MX): per block of 32 elements the E8M0 scale X = 2^(floor(log2
+ * amax) - 2) (E2M1's largest exponent is 2; X = 1 when amax is 0), elements e2m1(x / X),
+ * element 2j in the low nibble of byte j. */
+void orc_quant_mxfp4_key(int D, const uint16_t* x, uint8_t* packed, uint8_t* e8m0) {
+  memset(packed, 0, (size_t)D / 2);
+  for (int b = 0; b < D / 32; ++b) {
+    const float amax = amax_bf16(32, x + 32 * b);
+    int E = 127;
+    if (amax > 0.f) {
+      int e;
+      frexpf(amax, &e);  /* amax = m 2^e, m in [0.5, 1): floor(log2 amax) = e - 1 */
+      E = (e - 1) - 2 + 127;
+      if (E < 0) E = 0;
+      if (E > 254) E = 254;
+    }
+    e8m0[b] = (uint8_t)E;
+    const float X = ldexpf(1.0f, E - 127);
+    for (int i = 0; i < 32; ++i) {
+      const int d = 32 * b + i;
+      const uint8_t nib = orc_quant_e2m1(bf16f(x[d]) / X);
+      packed[d / 2] |= (uint8_t)((d & 1) ? nib << 4 : nib);
+    }
+  }
+}
+
+/* One NVFP4 latent: per block of 16 elements the E4M3 block scale bs = e4m3((amax / 6) / ts)
+ * with ts the fp32 tensor scale; elements e2m1(x / (bs * ts)) (0 when bs * ts is 0); element
+ * 2j in the low nibble of byte j. */
+void orc_quant_nvfp4_latent(int D, const uint16_t* x, float ts, uint8_t* packed, uint8_t* bscale) {
+  memset(packed, 0, (size_t)D / 2);
+  for (int b = 0; b < D / 16; ++b) {
+    const float amax = amax_bf16(16, x + 16 * b);
+    const uint8_t bs = orc_quant_e4m3((amax / 6.0f) / ts);
+    bscale[b] = bs;
+    const float sd = (float)orc_e4m3(bs) * ts;
+    for (int i = 0; i < 16; ++i) {
+      const int d = 16 * b + i;
+      const uint8_t nib = sd > 0.f ? orc_quant_e2m1(bf16f(x[d]) / sd) : 0;
+      packed[d / 2] |= (uint8_t)((d & 1) ? nib << 4 : nib);
+    }
+  }
+}
+
+/* Indexer query of one row: per head h a scale s_h = amax_h / 448 (1 when amax_h is 0), codes
+ * e4m3(q / s_h), and the head weight w'_h = w_h * s_h (fp32), so that
+ * w'_h ReLU(q'_h . k) = w_h ReLU(s_h q'_h . k) ~ w_h ReLU(q_h . k). */
+void orc_quantize_query(int H, int D, const uint16_t* q, const float* w, uint8_t* codes,
+                        float* wout) {
+  for (int h = 0; h < H; ++h) {
+    float s;
+    orc_quant_fp8_token(D, q + (size_t)h * D, codes + (size_t)h * D, &s);
+    wout[h] = w[h] * s;
+  }
 }
