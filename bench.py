@@ -19,6 +19,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -127,6 +129,48 @@ def cpu_baseline(cfg: int, wl, budget_s: float = 15.0):
                       f"top-k by sort, fp64 attention), {spent:.1f} s on {threads} threads"}
 
 
+def time_front(wl, d, kv, steps: int):
+    """Event time of the step before the path for one batch: every row's own new token quantised
+    into its pool row (index key and latent, dsa_cache_append) and the rows' indexer queries
+    quantised with the scale folded into the head weights (dsa_quantize_query).  Inputs are seeded
+    N(0, 1) bf16 values already on the device."""
+    import torch
+    import sparse_attention_decode_amd as sad
+    R = wl.num_rows
+    pos = wl.row_pos.astype(np.int64)
+    slots = wl.block_table[wl.row_seq, pos // wl.block_size].astype(np.int64) * wl.block_size \
+        + pos % wl.block_size
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + 17)
+    bf = lambda *shape: torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    d_slot = torch.from_numpy(slots).cuda()
+    ikey, lat, q = bf(R, 128), bf(R, 576), bf(R, 32, 128)
+    w = torch.randn(R, 32, generator=g, device="cuda")
+    q_idx = torch.empty(R, 32, 128, dtype=torch.uint8, device="cuda")
+    w_out = torch.empty_like(w)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        sad.dsa_cache_append(kv, d["pool"], d_slot, index_key=ikey, latent=lat)
+        sad.dsa_quantize_query(q, w, q_idx, w_out)
+
+    for _ in range(5):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / steps
+    key_b = 132 if wl.ikey_fmt == 0 else 68
+    lat_b = 580 if wl.lat_fmt == 0 else 324
+    nbytes = R * (8 + 2 * 128 + 2 * 576 + key_b + lat_b) + R * 32 * (2 * 128 + 4 + 128 + 4)
+    return {"entry_points": "dsa_cache_append + dsa_quantize_query", "new_tokens": R,
+            "query_rows": R, "us_per_step": us, "algorithmic_bytes_per_step": nbytes,
+            "achieved_GBps": nbytes / (us * 1e-6) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,7 +208,7 @@ def main():
     reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2}[cfg]
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    wls, devs, layers = [], [], []
+    wls, devs, layers, kvs = [], [], [], []
     for rep in range(reps):
         wl = synth.decode_config(cfg, replica=rep)
         kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
@@ -176,6 +220,7 @@ def main():
         wls.append(wl)
         devs.append(d)
         layers.append(layer)
+        kvs.append(kv)
         log(f"[bench] staged replica {rep} of {wl.name}: pool {d['pool'].numel() / 2**30:.2f} GiB")
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s")
@@ -264,6 +309,8 @@ def main():
                       "frac_of_8TBps": layer_gbps / PEAK_HBM_GBPS},
         "roofline": roof,
     }
+    # the step before the path, timed on its own after the layer (not part of `value`)
+    result["front"] = time_front(wl, devs[0], kvs[0], max(10, min(args.steps, 100)))
     if not args.no_cpu:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_budget)

@@ -204,6 +204,44 @@ DSA_API dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool,
                               float softmax_scale, uint16_t* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * The step before the path ("vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Low-latency decode:
+ * a fused DSA decode path: the indexer query is quantised with the head weights folded in, and the
+ * new token's index key and latent go into the KV cache, the latent write overlapping the
+ * indexer).  Rounding is to the nearest code, ties to the even code, saturating at the format's
+ * largest finite value; inputs must be finite.  The codes are exact functions of the bf16 inputs.
+ *
+ * dsa_cache_append — quantise num_tokens new tokens into their pool rows (formats as in
+ * dsa_kv_layout):
+ *   FP8 index key / FP8 latent: per-token scale amax / 448 (1 when amax is 0), codes E4M3(x / s)
+ *   MXFP4 index key: per 32 elements E8M0 exponent floor(log2 amax) - 2 (127 when amax is 0),
+ *     codes E2M1(x / 2^(E-127))
+ *   NVFP4 latent: per 16 elements block scale E4M3((amax / 6) / tensor scale), codes
+ *     E2M1(x / (block scale * tensor scale)) (0 when that product is 0)
+ *   slot      [num_tokens] int64 physical pool rows (block * block_size + slot in block, the
+ *             numbering of dsa_topk's phys); a negative entry or one >= num_blocks * block_size
+ *             is skipped (nothing written)
+ *   index_key [num_tokens][128] bf16 or NULL (keys not written);  latent [num_tokens][576] bf16
+ *             or NULL (latents not written): a caller can write the keys before the scorer and
+ *             the latents on another stream while it runs
+ * Two entries naming one slot race.  Returns INVALID_ARG for a bad layout, pointer or alignment
+ * (slot 8-byte, index_key 4-byte, latent 8-byte aligned).
+ */
+DSA_API dsa_status dsa_cache_append(const dsa_kv_layout* kv, void* pool, int32_t num_tokens,
+                                    const int64_t* slot, const uint16_t* index_key,
+                                    const uint16_t* latent, void* stream);
+
+/*
+ * dsa_quantize_query — the indexer query in the form dsa_indexer_scores reads: per row r and
+ * head h, s = amax_h / 448 (1 when amax_h is 0), q_idx[r][h] = E4M3(q[r][h] / s) and
+ * w_out[r][h] = w[r][h] * s (so w_out ReLU(q_idx . k) = w ReLU(s q_idx . k)).
+ *   q [num_rows][32][128] bf16 (4-byte aligned);  w [num_rows][32] fp32
+ *   q_idx [num_rows][32][128] E4M3 output (2-byte aligned);  w_out [num_rows][32] fp32 output
+ *   (w_out may be w)
+ */
+DSA_API dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const float* w,
+                                      uint8_t* q_idx, float* w_out, void* stream);
+
 /* Text of a status code, and the calling thread's last error message ("" if none). */
 DSA_API const char* dsa_status_string(dsa_status s);
 DSA_API const char* dsa_last_error(void);

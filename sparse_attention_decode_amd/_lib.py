@@ -18,7 +18,8 @@ MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 # Every symbol include/dsa.h declares.
 EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
            "sparse_mla_workspace_bytes",
-           "sparse_mla_decode", "sparse_mla_prefill", "dsa_status_string", "dsa_last_error")
+           "sparse_mla_decode", "sparse_mla_prefill", "dsa_cache_append", "dsa_quantize_query",
+           "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -78,6 +79,10 @@ def lib():
             f.restype = i32
             f.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp, vp, vp, i32,
                           f32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dsa_cache_append.restype = i32
+        L.dsa_cache_append.argtypes = [ctypes.POINTER(KVLayout), vp, i32, vp, vp, vp, vp]
+        L.dsa_quantize_query.restype = i32
+        L.dsa_quantize_query.argtypes = [i32, vp, vp, vp, vp, vp]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [i32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -172,3 +177,18 @@ def sparse_mla_prefill(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None,
                        stream=None, phys=None):
     _mla("sparse_mla_prefill", kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse,
          workspace, stream)
+
+
+def dsa_cache_append(kv: KVLayout, pool, slot, index_key=None, latent=None, stream=None):
+    """Quantise new tokens into their pool rows.  slot: int64 [n] physical rows; index_key: bf16
+    [n, 128] or None; latent: bf16 [n, 576] or None."""
+    _check(lib().dsa_cache_append(ctypes.byref(kv), _ptr(pool), slot.numel(), _ptr(slot),
+                                  _ptr(index_key), _ptr(latent), _stream(stream)),
+           "dsa_cache_append")
+
+
+def dsa_quantize_query(q, w, q_idx, w_out, stream=None):
+    """q: bf16 [R, 32, 128], w: f32 [R, 32] -> q_idx: uint8 E4M3 [R, 32, 128], w_out: f32 [R, 32]
+    (w_out may be w)."""
+    _check(lib().dsa_quantize_query(q.shape[0], _ptr(q), _ptr(w), _ptr(q_idx), _ptr(w_out),
+                                    _stream(stream)), "dsa_quantize_query")

@@ -291,4 +291,40 @@ dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const d
                     workspace_bytes, static_cast<hipStream_t>(stream), true);
 }
 
+dsa_status dsa_cache_append(const dsa_kv_layout* kv, void* pool, int32_t num_tokens,
+                            const int64_t* slot, const uint16_t* index_key, const uint16_t* latent,
+                            void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_layout(kv, pool);
+  if (st != DSA_OK) return st;
+  if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0 || (!index_key && !latent)) return DSA_OK;
+  if (!slot) return fail(DSA_ERR_INVALID_ARG, "slot must be non-NULL");
+  if (!aligned(slot, 8) || (index_key && !aligned(index_key, 4)) ||
+      (latent && !aligned(latent, 8)))
+    return fail(DSA_ERR_INVALID_ARG,
+                "slot must be 8-byte, index_key 4-byte and latent 8-byte aligned");
+  const float ts = kv->latent_format == DSA_LATENT_NVFP4 ? kv->latent_tensor_scale : 1.f;
+  return hip_status(dsa::launch_cache_write(pool_view(kv, pool), static_cast<uint8_t*>(pool),
+                                            kv->ikey_format, kv->latent_format, ts, num_tokens,
+                                            slot, index_key, latent,
+                                            static_cast<hipStream_t>(stream)),
+                    "dsa_cache_append launch");
+}
+
+dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const float* w, uint8_t* q_idx,
+                              float* w_out, void* stream) {
+  g_err[0] = 0;
+  if (num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "num_rows must be >= 0");
+  if (num_rows > (1 << 25)) return fail(DSA_ERR_INVALID_ARG, "num_rows too large");
+  if (num_rows == 0) return DSA_OK;
+  if (!q || !w || !q_idx || !w_out)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, q_idx and w_out must be non-NULL");
+  if (!aligned(q, 4) || !aligned(w, 4) || !aligned(q_idx, 2) || !aligned(w_out, 4))
+    return fail(DSA_ERR_INVALID_ARG, "q, w, w_out must be 4-byte and q_idx 2-byte aligned");
+  return hip_status(dsa::launch_quantize_query(num_rows, q, w, q_idx, w_out,
+                                               static_cast<hipStream_t>(stream)),
+                    "dsa_quantize_query launch");
+}
+
 }  // extern "C"

@@ -79,4 +79,11 @@ int mla_num_splits(int32_t num_rows, int32_t k, bool invariant);
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant);
 hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s);
 
+// The step before the path: quantise new tokens into their pool rows, and the indexer query.
+hipError_t launch_cache_write(const PoolView& pool, uint8_t* base, int ikey_fmt, int lat_fmt,
+                              float tensor_scale, int32_t n, const int64_t* slot,
+                              const uint16_t* ikey, const uint16_t* latent, hipStream_t s);
+hipError_t launch_quantize_query(int32_t num_rows, const uint16_t* q, const float* w, uint8_t* qo,
+                                 float* wo, hipStream_t s);
+
 }  // namespace dsa

@@ -153,3 +153,35 @@ def test_empty_batch_is_a_no_op():
     for fn in (lib.sparse_mla_decode, lib.sparse_mla_prefill):
         assert fn(ctypes.byref(kv), pool, ctypes.byref(b), p, p, p, 2048, 0.1, p, None, None, 0,
                   None) == L.DSA_OK
+
+
+def test_front_entry_points_validate_before_launch():
+    # dsa_cache_append / dsa_quantize_query: bad arguments are rejected on the host and nothing-to-
+    # do calls return DSA_OK, all without a launch (no GPU here).
+    lib = L.lib()
+    kv = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_NVFP4, 10, 0.5)
+    pool = ctypes.c_void_p(0x100000)
+    p = ctypes.c_void_p(0x2000)
+    ok, bad = L.DSA_OK, L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_cache_append(ctypes.byref(kv), None, 4, p, p, p, None) == bad
+    assert lib.dsa_cache_append(None, pool, 4, p, p, p, None) == bad
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, -1, p, p, p, None) == bad
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 4, None, p, p, None) == bad
+    assert b"slot" in lib.dsa_last_error()
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 4, ctypes.c_void_p(0x2004), p, p,
+                                None) == bad
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 4, p, ctypes.c_void_p(0x2002), None,
+                                None) == bad
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 4, p, None, ctypes.c_void_p(0x2004),
+                                None) == bad
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 0, None, p, p, None) == ok
+    assert lib.dsa_cache_append(ctypes.byref(kv), pool, 4, p, None, None, None) == ok
+    kvb = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    kvb.block_size = 32
+    assert lib.dsa_cache_append(ctypes.byref(kvb), pool, 4, p, p, p, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_quantize_query(-1, p, p, p, p, None) == bad
+    assert lib.dsa_quantize_query(2, None, p, p, p, None) == bad
+    assert lib.dsa_quantize_query(2, p, p, p, None, None) == bad
+    assert lib.dsa_quantize_query(2, ctypes.c_void_p(0x2002), p, p, p, None) == bad
+    assert lib.dsa_quantize_query(2, p, p, ctypes.c_void_p(0x2001), p, None) == bad
+    assert lib.dsa_quantize_query(0, None, None, None, None, None) == ok
