@@ -171,6 +171,96 @@ def time_front(wl, d, kv, steps: int):
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9}
 
 
+def bench_dcp(args):
+    """The decode step under emulated decode context parallelism: the workload's sequences split
+    into W token-interleaved shards (each its own pool), per shard the scorer and the local
+    select, then the publish of the sorted local lists, the exact merge, per shard the attention
+    over its part, and the LSE combine.  On one GPU the shards run one after another; `value` is
+    rows/s of the whole emulated step, and the merge and combine are timed with events."""
+    import torch
+    import sparse_attention_decode_amd as sad
+    import synth
+    import synth.device
+    W = args.dcp
+    if not 1 <= W <= sad.MAX_SHARDS:
+        sys.exit(f"--dcp must be in [1, {sad.MAX_SHARDS}]")
+    variant = {"packed": sad.MERGE_PACKED, "scores": sad.MERGE_SCORES,
+               "generic": sad.MERGE_GENERIC}[args.dcp_variant]
+    wl = synth.decode_config(args.config)
+    if int(np.diff(wl.seq_row_start).max()) > sad.MAX_ROWS_PER_SEQ:
+        sys.exit("--dcp emulates the decode path (up to 8 rows per sequence)")
+    R, k = wl.num_rows, wl.k
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    shards = []
+    for r in range(W):
+        sw = synth.shard_workload(wl, W, r)
+        kv = sad.kv_layout(sw.ikey_fmt, sw.lat_fmt, sw.num_blocks, sw.lat_tensor_scale)
+        d = synth.device.stage(sw, kv.as_dict())
+        batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
+                                d["max_rows_per_seq"], d["max_context"])
+        shards.append((kv, d, batch, sad.DSALayer(kv, batch, k, wl.softmax_scale)))
+        log(f"[bench] staged shard {r} of {W}: pool {d['pool'].numel() / 2**30:.2f} GiB")
+    dev = dict(device="cuda")
+    mb = torch.empty(sad.dsa_dcp_mailbox_bytes(R, k, W), dtype=torch.uint8, **dev)
+    parts = torch.empty(sad.dsa_dcp_partials_bytes(R, k, W), dtype=torch.uint8, **dev)
+    idx = torch.empty((R, k), dtype=torch.int32, **dev)
+    cnt = torch.empty(R, dtype=torch.int32, **dev)
+    sidx = torch.empty((W, R, k), dtype=torch.int32, **dev)
+    scnt = torch.empty((W, R), dtype=torch.int32, **dev)
+    stats = torch.empty((R, 4), dtype=torch.int32, **dev)
+    out = torch.empty((R, sad.MLA_HEADS, sad.MLA_DV), dtype=torch.bfloat16, **dev)
+    lse = torch.empty((R, sad.MLA_HEADS), dtype=torch.float32, **dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for r, (kv, d, batch, layer) in enumerate(shards):
+            layer.scores_step(d["pool"], d["q_idx"], d["w"])
+            layer.topk_step(phys=False)
+            sad.dsa_dcp_publish(k, W, r, layer.scores, layer.idx, layer.count, mb)
+        if ev is not None:
+            ev[0].record(stream)
+        sad.dsa_dcp_merge(k, W, variant, mb, idx, cnt, sidx, scnt, stats)
+        if ev is not None:
+            ev[1].record(stream)
+        for r, (kv, d, batch, layer) in enumerate(shards):
+            sad.sparse_mla_decode_shard(kv, d["pool"], batch, d["q"], sidx[r], k,
+                                        wl.softmax_scale, r, W, parts, count=scnt[r])
+        if ev is not None:
+            ev[2].record(stream)
+        sad.dsa_lse_combine(R, k, W, parts, out, lse)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    merge_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    comb_us = 1e3 * sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    st = stats.cpu().numpy()
+    generic = W * np.minimum(k, np.ceil((wl.row_pos + 1) / W)) * 8
+    print(json.dumps({
+        "metric": "DSA decode layer query-tokens/s under emulated decode context parallelism "
+                  "(all shards on one GPU, exact merge)",
+        "value": R * args.steps / elapsed, "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "data": "synthetic (seeded, exact-grid FP8 keys)",
+        "config": {"workload": wl.name, "shards": W, "variant": args.dcp_variant, "rows": R,
+                   "context": int(wl.seq_len.max()), "top_k": k},
+        "merge": {"us": merge_us, "rounds_max": int(st[:, 0].max()),
+                  "resending_shards": int(st[:, 1].sum()), "tie_entries": int(st[:, 2].sum()),
+                  "bytes_per_row_mean": float(st[:, 3].mean()),
+                  "bytes_per_row_per_shard_mean": float(st[:, 3].mean() / W),
+                  "generic_bytes_per_row_mean": float(generic.mean())},
+        "combine_us": comb_us,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +271,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--dcp", type=int, default=0,
+                    help="emulate decode context parallelism: the workload split into this many "
+                         "token-interleaved shards on the one GPU, merged exactly (prints its own "
+                         "JSON line instead of the layer's)")
+    ap.add_argument("--dcp-variant", choices=["packed", "scores", "generic"], default="packed")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run three 1 GiB device-to-device copies (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -203,6 +298,10 @@ def main():
     import sparse_attention_decode_amd as sad
     import synth
     import synth.device
+
+    if args.dcp:
+        bench_dcp(args)
+        return
 
     cfg = args.config
     reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2}[cfg]

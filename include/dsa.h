@@ -242,6 +242,89 @@ DSA_API dsa_status dsa_cache_append(const dsa_kv_layout* kv, void* pool, int32_t
 DSA_API dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const float* w,
                                       uint8_t* q_idx, float* w_out, void* stream);
 
+/*
+ * Decode context parallelism, emulated on one GPU ("vLLM Delivers Day-0 Support for Kimi K3.1
+ * Pro", §Long context: decode context parallelism with a sparse indexer; §An exact top-k merge with
+ * 10x less traffic; §AMD / Communication: Efficient cross-GPU communication).  Shard r of W holds
+ * tokens r, r + W, r + 2W, ... of each sequence in a pool of its own (token j of the shard is
+ * token j W + r of the sequence); a row at position p sees the shard's tokens [0, (p - r) / W].
+ * One layer step: per shard, dsa_indexer_scores and dsa_topk (k) on that shard, then
+ * dsa_dcp_publish; then dsa_dcp_merge once (every shard would run the same select on the same
+ * gathered messages); then, per shard, sparse_mla_decode_shard over its part of the selection
+ * (shard_idx[r]); then dsa_lse_combine.  The selected set equals the top-k of the whole sequence
+ * (score descending, token index ascending) exactly, in every message variant.
+ *
+ * Message variants of the merge (what each shard sends per row):
+ *   DSA_MERGE_PACKED  its best min(k, ceil(1.5 k / W)) candidates, 32 bits each: the upper 16 bits
+ *                     of the score's order-preserving key and the candidate's 16-bit rank in its
+ *                     own list (the page's packed candidates)
+ *   DSA_MERGE_SCORES  its whole local top-k as fp32 scores; token indices stay local (the AMD
+ *                     section's score-only exchange)
+ *   DSA_MERGE_GENERIC its whole local top-k as (fp32 score, index) pairs (the generic merge)
+ * The select finds the k-th largest message key.  A shard that sent fewer candidates than it holds
+ * and whose weakest sent candidate reaches that threshold resends its full local top-k, and the
+ * select is redone (at most once).  Entries equal to the threshold key, when only some of them are
+ * needed, are ordered exactly by (score, index) from a second small exchange of their score and
+ * index.
+ */
+enum { DSA_MERGE_PACKED = 0, DSA_MERGE_SCORES = 1, DSA_MERGE_GENERIC = 2, DSA_MAX_SHARDS = 8 };
+
+/* Bytes of the mailbox (the exchange buffer the shards' lists go to) for num_rows rows, top-k k
+ * and num_shards shards (0 for an out-of-range argument). */
+DSA_API size_t dsa_dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards);
+
+/* Shard `shard` publishes each row's local top-k, sorted by score descending and local index
+ * ascending, with global token indices (local * num_shards + shard).
+ *   scores/ld_scores: that shard's dsa_indexer_scores output;  idx/count: its dsa_topk output (k)
+ *   mailbox: at least dsa_dcp_mailbox_bytes(num_rows, k, num_shards) bytes, 16-byte aligned; the
+ *   calls for all shards (any order) must complete before dsa_dcp_merge reads it. */
+DSA_API dsa_status dsa_dcp_publish(int32_t num_rows, int32_t k, int32_t num_shards, int32_t shard,
+                                   const float* scores, int64_t ld_scores, const int32_t* idx,
+                                   const int32_t* count, void* mailbox, size_t mailbox_bytes,
+                                   void* stream);
+
+/* The exact merge.  Outputs:
+ *   idx   [num_rows][k] global token indices ascending, then -1;  count [num_rows]
+ *   shard_idx   [num_shards][num_rows][k] each shard's selected LOCAL indices ascending, then -1
+ *               (the idx argument of that shard's sparse_mla_decode);  shard_count [num_shards][num_rows]
+ *   stats [num_rows][4] or NULL: rounds (1, or 2 after a resend), shards that resent, entries of
+ *         the tie exchange (0 if none), bytes all shards sent for the row over all rounds. */
+DSA_API dsa_status dsa_dcp_merge(int32_t num_rows, int32_t k, int32_t num_shards, int32_t variant,
+                                 void* mailbox, size_t mailbox_bytes, int32_t* idx, int32_t* count,
+                                 int32_t* shard_idx, int32_t* shard_count, int32_t* stats,
+                                 void* stream);
+
+/* Bytes of the partials buffer that sparse_mla_decode_shard fills and dsa_lse_combine reads, for
+ * num_rows rows, top-k k, num_shards shards and dsa_batch.flags `flags` (0 for a bad argument). */
+DSA_API size_t dsa_dcp_partials_bytes(int32_t num_rows, int32_t k, int32_t num_shards,
+                                      uint32_t flags);
+
+/* One shard's attention over its part of the selection (idx = that shard's shard_idx, local
+ * indices; count = its shard_count, or NULL; kv/pool/batch: the shard's own pool and batch; phys
+ * NULL, or the shard's pool rows).  Arguments as sparse_mla_decode, except that nothing is written
+ * to an output: the row's splits (fp16 outputs normalised and scaled by a power of two per head,
+ * with their base-2 LSE) go to the shard's slots of `partials`, so the calls of all shards (in any
+ * order) fill the buffer for one dsa_lse_combine.  The shard's split count is sized for k /
+ * num_shards tokens; with count, each row's count entries are spread evenly over the splits (no
+ * split walks the -1 tail), without it the splits cover all k slots. */
+DSA_API dsa_status sparse_mla_decode_shard(const dsa_kv_layout* kv, const void* pool,
+                                           const dsa_batch* batch, const uint16_t* q,
+                                           const int32_t* idx, const int32_t* count,
+                                           const int32_t* phys, int32_t k,
+                                           float softmax_scale, int32_t shard, int32_t num_shards,
+                                           void* partials, size_t partials_bytes, void* stream);
+
+/* Log-sum-exp merge of all shards' partial attention results (page: partial outputs combined by
+ * their LSE): for each row and head, over every split slot s of every shard with LSE l_s (natural
+ * log here), M = max l_s, out = sum_s e^(l_s - M) o_s / sum_s e^(l_s - M) (bf16, fp32
+ * accumulation in slot order), lse = M + ln(sum_s e^(l_s - M)); out = 0 and lse = -inf where no
+ * shard selected a token.  k, num_shards and flags must be those of the shard calls; lse may be
+ * NULL.  The exchanged partials take as many bytes as bf16 outputs but keep 11 significant bits
+ * relative to the head's largest value, so the merged output keeps the single-GPU precision. */
+DSA_API dsa_status dsa_lse_combine(int32_t num_rows, int32_t k, int32_t num_shards, uint32_t flags,
+                                   const void* partials, size_t partials_bytes, uint16_t* out,
+                                   float* lse, void* stream);
+
 /* Text of a status code, and the calling thread's last error message ("" if none). */
 DSA_API const char* dsa_status_string(dsa_status s);
 DSA_API const char* dsa_last_error(void);

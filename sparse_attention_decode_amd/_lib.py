@@ -19,7 +19,9 @@ MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
            "sparse_mla_workspace_bytes",
            "sparse_mla_decode", "sparse_mla_prefill", "dsa_cache_append", "dsa_quantize_query",
-           "dsa_status_string", "dsa_last_error")
+           "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_dcp_partials_bytes",
+           "sparse_mla_decode_shard", "dsa_lse_combine", "dsa_status_string", "dsa_last_error")
+MERGE_PACKED, MERGE_SCORES, MERGE_GENERIC, MAX_SHARDS = 0, 1, 2, 8
 
 
 class DSAError(RuntimeError):
@@ -83,6 +85,20 @@ def lib():
         L.dsa_cache_append.argtypes = [ctypes.POINTER(KVLayout), vp, i32, vp, vp, vp, vp]
         L.dsa_quantize_query.restype = i32
         L.dsa_quantize_query.argtypes = [i32, vp, vp, vp, vp, vp]
+        sz = ctypes.c_size_t
+        L.dsa_dcp_mailbox_bytes.restype = sz
+        L.dsa_dcp_mailbox_bytes.argtypes = [i32, i32, i32]
+        L.dsa_dcp_publish.restype = i32
+        L.dsa_dcp_publish.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, sz, vp]
+        L.dsa_dcp_merge.restype = i32
+        L.dsa_dcp_merge.argtypes = [i32, i32, i32, i32, vp, sz, vp, vp, vp, vp, vp, vp]
+        L.dsa_dcp_partials_bytes.restype = sz
+        L.dsa_dcp_partials_bytes.argtypes = [i32, i32, i32, ctypes.c_uint32]
+        L.sparse_mla_decode_shard.restype = i32
+        L.sparse_mla_decode_shard.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch),
+                                              vp, vp, vp, vp, i32, f32, i32, i32, vp, sz, vp]
+        L.dsa_lse_combine.restype = i32
+        L.dsa_lse_combine.argtypes = [i32, i32, i32, ctypes.c_uint32, vp, sz, vp, vp, vp]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [i32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -192,3 +208,52 @@ def dsa_quantize_query(q, w, q_idx, w_out, stream=None):
     (w_out may be w)."""
     _check(lib().dsa_quantize_query(q.shape[0], _ptr(q), _ptr(w), _ptr(q_idx), _ptr(w_out),
                                     _stream(stream)), "dsa_quantize_query")
+
+
+def dsa_dcp_mailbox_bytes(num_rows: int, k: int, num_shards: int) -> int:
+    return int(lib().dsa_dcp_mailbox_bytes(num_rows, k, num_shards))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def dsa_dcp_publish(k: int, num_shards: int, shard: int, scores, idx, count, mailbox,
+                    stream=None):
+    """Shard `shard` publishes its rows' sorted local top-k (scores [R, ld] f32, idx [R, k] and
+    count [R] from dsa_topk on that shard) into the mailbox (uint8 device tensor)."""
+    _check(lib().dsa_dcp_publish(count.numel(), k, num_shards, shard, _ptr(scores),
+                                 scores.stride(0), _ptr(idx), _ptr(count), _ptr(mailbox),
+                                 _nbytes(mailbox), _stream(stream)), "dsa_dcp_publish")
+
+
+def dsa_dcp_merge(k: int, num_shards: int, variant: int, mailbox, idx, count, shard_idx,
+                  shard_count, stats=None, stream=None):
+    """The exact merge: idx [R, k], count [R], shard_idx [W, R, k], shard_count [W, R] (int32),
+    stats [R, 4] int32 or None."""
+    _check(lib().dsa_dcp_merge(count.numel(), k, num_shards, variant, _ptr(mailbox),
+                               _nbytes(mailbox), _ptr(idx), _ptr(count), _ptr(shard_idx),
+                               _ptr(shard_count), _ptr(stats), _stream(stream)), "dsa_dcp_merge")
+
+
+def dsa_dcp_partials_bytes(num_rows: int, k: int, num_shards: int, flags: int = 0) -> int:
+    return int(lib().dsa_dcp_partials_bytes(num_rows, k, num_shards, flags))
+
+
+def sparse_mla_decode_shard(kv, pool, batch, q, idx, k, softmax_scale, shard: int,
+                            num_shards: int, partials, count=None, stream=None, phys=None):
+    """One shard's attention over its part of the selection (idx / count: its shard_idx /
+    shard_count rows), into its slots of `partials`."""
+    _check(lib().sparse_mla_decode_shard(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c),
+                                         _ptr(q), _ptr(idx), _ptr(count), _ptr(phys), k,
+                                         softmax_scale, shard,
+                                         num_shards, _ptr(partials), _nbytes(partials),
+                                         _stream(stream)), "sparse_mla_decode_shard")
+
+
+def dsa_lse_combine(num_rows: int, k: int, num_shards: int, partials, out, lse=None, flags=0,
+                    stream=None):
+    """Merge every shard's partials into out bf16 [R, 96, 512] (and lse f32 [R, 96])."""
+    _check(lib().dsa_lse_combine(num_rows, k, num_shards, flags, _ptr(partials),
+                                 _nbytes(partials), _ptr(out), _ptr(lse), _stream(stream)),
+           "dsa_lse_combine")

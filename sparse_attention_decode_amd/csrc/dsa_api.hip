@@ -1,6 +1,8 @@
 // C ABI of the DSA layer: argument validation, pool layout, and kernel dispatch on the caller's
 // stream.  Declarations and argument contracts are in include/dsa.h.
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -92,17 +94,62 @@ dsa::BatchView batch_view(const dsa_batch* b) {
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Split count and split size of the decode attention for num_rows rows and top-k k.
+void mla_splits(int32_t num_rows, int32_t k, bool invariant, int32_t* nsplit, int32_t* per) {
+  int32_t ns = dsa::mla_num_splits(num_rows, k, invariant);
+  *per = (int32_t)align_up((k + ns - 1) / ns, 32);
+  *nsplit = (k + *per - 1) / *per;
+}
+
+// Splits of one shard's attention under decode context parallelism: sized for the shard's
+// expected share of the selection (k / num_shards), since each shard's entries are compacted at
+// the front of its list and spread over its splits by count.
+void shard_splits(int32_t num_rows, int32_t k, int32_t num_shards, bool invariant,
+                  int32_t* nsplit, int32_t* per) {
+  int32_t ns, unused;
+  if (invariant)
+    mla_splits(num_rows, k, true, &ns, &unused);
+  else
+    mla_splits(num_rows, std::max(32, (k + num_shards - 1) / num_shards), false, &ns, &unused);
+  *per = (int32_t)align_up((k + ns - 1) / ns, 32);  // ranges covering all k when no count is given
+  *nsplit = (k + *per - 1) / *per;
+}
+
+size_t partial_bytes(int32_t num_rows, int32_t slots) {
+  return (size_t)num_rows * slots * DSA_MLA_HEADS *
+         (DSA_MLA_DV * sizeof(uint16_t) + 2 * sizeof(float));
+}
+
+void partial_views(dsa::MlaArgs& a, void* buf, int32_t num_rows) {
+  const size_t nslot = (size_t)num_rows * a.split_slots * DSA_MLA_HEADS;
+  a.part_o = static_cast<uint16_t*>(buf);
+  a.part_lse = reinterpret_cast<float*>(a.part_o + nslot * DSA_MLA_DV);
+  a.part_exp = reinterpret_cast<int32_t*>(a.part_lse + nslot);
+}
+
+// shard < 0: the whole attention of each row (decode or prefill variant).  shard >= 0: the part of
+// decode context parallelism one shard runs: its splits go to partial slots [shard * nsplit,
+// (shard + 1) * nsplit) of a buffer holding num_shards * nsplit slots per row (workspace), and no
+// output is written (dsa_lse_combine writes it).
 dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
                       const uint16_t* q, const int32_t* idx, const int32_t* phys, int32_t k,
                       float softmax_scale,
                       uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, bool prefill) {
+                      hipStream_t stream, bool prefill, int32_t shard = -1,
+                      int32_t num_shards = 1, const int32_t* count = nullptr) {
   dsa_status st = check_layout(kv, pool);
   if (st != DSA_OK) return st;
   if ((st = check_batch(batch)) != DSA_OK) return st;
-  if (!q || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-NULL");
-  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
-    return fail(DSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (shard >= 0) {
+    if (num_shards < 1 || num_shards > DSA_MAX_SHARDS || shard >= num_shards)
+      return fail(DSA_ERR_INVALID_ARG, "shard %d of %d shards out of range", shard, num_shards);
+    if (!q || !idx) return fail(DSA_ERR_INVALID_ARG, "q and idx must be non-NULL");
+    if (!aligned(q, 16)) return fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  } else {
+    if (!q || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+      return fail(DSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  }
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
   if (!isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale not finite");
   if (batch->num_rows == 0) return DSA_OK;
@@ -118,25 +165,33 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.out = out;
   a.lse = lse;
   const bool invariant = (batch->flags & DSA_BATCH_INVARIANT) != 0;
-  a.nsplit = (prefill && !invariant) ? 1 : dsa::mla_num_splits(batch->num_rows, k, invariant);
-  a.tokens_per_split = (int32_t)align_up((k + a.nsplit - 1) / a.nsplit, 32);
-  a.nsplit = (k + a.tokens_per_split - 1) / a.tokens_per_split;
+  a.count = count;
+  if (shard >= 0) {
+    shard_splits(batch->num_rows, k, num_shards, invariant, &a.nsplit, &a.tokens_per_split);
+  } else if (prefill && !invariant) {
+    a.nsplit = 1;
+    a.tokens_per_split = (int32_t)align_up(k, 32);
+  } else {
+    mla_splits(batch->num_rows, k, invariant, &a.nsplit, &a.tokens_per_split);
+  }
+  a.split_base = shard >= 0 ? shard * a.nsplit : 0;
+  a.split_slots = shard >= 0 ? num_shards * a.nsplit : a.nsplit;
+  a.out_direct = shard < 0 && a.nsplit == 1;
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.part_exp = nullptr;
-  if (a.nsplit > 1) {
-    const size_t need = dsa::mla_workspace_bytes(batch->num_rows, k, invariant);
+  if (!a.out_direct) {
+    const size_t need = partial_bytes(batch->num_rows, a.split_slots);
     if (!workspace || workspace_bytes < need)
-      return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+      return fail(DSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu given",
+                  shard >= 0 ? "partials buffer" : "workspace", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
-    const size_t nslot = (size_t)batch->num_rows * a.nsplit * DSA_MLA_HEADS;
-    a.part_o = static_cast<uint16_t*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(a.part_o + nslot * DSA_MLA_DV);
-    a.part_exp = reinterpret_cast<int32_t*>(a.part_lse + nslot);
+    partial_views(a, workspace, batch->num_rows);
   }
-  return hip_status(dsa::launch_sparse_mla(a, kv->latent_format, stream),
-                    prefill ? "sparse_mla_prefill launch" : "sparse_mla_decode launch");
+  return hip_status(dsa::launch_sparse_mla(a, kv->latent_format, shard < 0, stream),
+                    shard >= 0 ? "sparse_mla_decode_shard launch"
+                               : (prefill ? "sparse_mla_prefill launch" : "sparse_mla_decode launch"));
 }
 
 }  // namespace
@@ -325,6 +380,117 @@ dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const float* 
   return hip_status(dsa::launch_quantize_query(num_rows, q, w, q_idx, w_out,
                                                static_cast<hipStream_t>(stream)),
                     "dsa_quantize_query launch");
+}
+
+size_t dsa_dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards) {
+  if (num_rows <= 0 || k < 1 || k > DSA_MAX_TOPK || num_shards < 1 ||
+      num_shards > DSA_MAX_SHARDS)
+    return 0;
+  return dsa::dcp_mailbox_bytes(num_rows, k, num_shards);
+}
+
+static dsa_status check_dcp(int32_t num_rows, int32_t k, int32_t num_shards, const void* mailbox,
+                            size_t mailbox_bytes) {
+  if (num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "num_rows must be >= 0");
+  if (num_rows > (1 << 20)) return fail(DSA_ERR_INVALID_ARG, "num_rows too large");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
+  if (num_shards < 1 || num_shards > DSA_MAX_SHARDS)
+    return fail(DSA_ERR_INVALID_ARG, "num_shards %d not in [1, %d]", num_shards, DSA_MAX_SHARDS);
+  if (num_rows == 0) return DSA_OK;
+  const size_t need = dsa::dcp_mailbox_bytes(num_rows, k, num_shards);
+  if (!mailbox || mailbox_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "mailbox of %zu bytes needed, %zu given", need,
+                mailbox ? mailbox_bytes : (size_t)0);
+  if (!aligned(mailbox, 16)) return fail(DSA_ERR_INVALID_ARG, "mailbox must be 16-byte aligned");
+  return DSA_OK;
+}
+
+dsa_status dsa_dcp_publish(int32_t num_rows, int32_t k, int32_t num_shards, int32_t shard,
+                           const float* scores, int64_t ld_scores, const int32_t* idx,
+                           const int32_t* count, void* mailbox, size_t mailbox_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_dcp(num_rows, k, num_shards, mailbox, mailbox_bytes);
+  if (st != DSA_OK || num_rows == 0) return st;
+  if (shard < 0 || shard >= num_shards)
+    return fail(DSA_ERR_INVALID_ARG, "shard %d not in [0, %d)", shard, num_shards);
+  if (!scores || !idx || !count)
+    return fail(DSA_ERR_INVALID_ARG, "scores, idx and count must be non-NULL");
+  if (ld_scores < 1) return fail(DSA_ERR_INVALID_ARG, "ld_scores must be positive");
+  return hip_status(dsa::launch_dcp_publish(num_rows, k, num_shards, shard, scores, ld_scores, idx,
+                                            count, mailbox, static_cast<hipStream_t>(stream)),
+                    "dsa_dcp_publish launch");
+}
+
+dsa_status dsa_dcp_merge(int32_t num_rows, int32_t k, int32_t num_shards, int32_t variant,
+                         void* mailbox, size_t mailbox_bytes, int32_t* idx, int32_t* count,
+                         int32_t* shard_idx, int32_t* shard_count, int32_t* stats, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_dcp(num_rows, k, num_shards, mailbox, mailbox_bytes);
+  if (st != DSA_OK || num_rows == 0) return st;
+  if (variant != DSA_MERGE_PACKED && variant != DSA_MERGE_SCORES && variant != DSA_MERGE_GENERIC)
+    return fail(DSA_ERR_INVALID_ARG, "unknown merge variant %d", variant);
+  if (!idx || !count || !shard_idx || !shard_count)
+    return fail(DSA_ERR_INVALID_ARG, "idx, count, shard_idx and shard_count must be non-NULL");
+  return hip_status(dsa::launch_dcp_merge(num_rows, k, num_shards, variant, mailbox, idx, count,
+                                          shard_idx, shard_count, stats,
+                                          static_cast<hipStream_t>(stream)),
+                    "dsa_dcp_merge launch");
+}
+
+size_t dsa_dcp_partials_bytes(int32_t num_rows, int32_t k, int32_t num_shards, uint32_t flags) {
+  if (num_rows <= 0 || k < 1 || k > DSA_MAX_TOPK || num_shards < 1 ||
+      num_shards > DSA_MAX_SHARDS)
+    return 0;
+  int32_t ns, per;
+  shard_splits(num_rows, k, num_shards, (flags & DSA_BATCH_INVARIANT) != 0, &ns, &per);
+  return partial_bytes(num_rows, num_shards * ns);
+}
+
+dsa_status sparse_mla_decode_shard(const dsa_kv_layout* kv, const void* pool,
+                                   const dsa_batch* batch, const uint16_t* q, const int32_t* idx,
+                                   const int32_t* count, const int32_t* phys, int32_t k,
+                                   float softmax_scale, int32_t shard, int32_t num_shards,
+                                   void* partials, size_t partials_bytes, void* stream) {
+  g_err[0] = 0;
+  if (shard < 0) return fail(DSA_ERR_INVALID_ARG, "shard %d out of range", shard);
+  return mla_common(kv, pool, batch, q, idx, phys, k, softmax_scale, nullptr, nullptr, partials,
+                    partials_bytes, static_cast<hipStream_t>(stream), false, shard, num_shards,
+                    count);
+}
+
+dsa_status dsa_lse_combine(int32_t num_rows, int32_t k, int32_t num_shards, uint32_t flags,
+                           const void* partials, size_t partials_bytes, uint16_t* out, float* lse,
+                           void* stream) {
+  g_err[0] = 0;
+  if (num_rows < 0 || num_rows > (1 << 20))
+    return fail(DSA_ERR_INVALID_ARG, "num_rows out of range");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
+  if (num_shards < 1 || num_shards > DSA_MAX_SHARDS)
+    return fail(DSA_ERR_INVALID_ARG, "num_shards %d not in [1, %d]", num_shards, DSA_MAX_SHARDS);
+  if (flags & ~DSA_BATCH_INVARIANT) return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
+  if (num_rows == 0) return DSA_OK;
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out must be non-NULL");
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  dsa::MlaArgs a = {};
+  a.batch.num_rows = num_rows;
+  a.k = k;
+  int32_t ns, per;
+  shard_splits(num_rows, k, num_shards, (flags & DSA_BATCH_INVARIANT) != 0, &ns, &per);
+  a.nsplit = ns;
+  a.tokens_per_split = per;
+  a.split_slots = num_shards * ns;
+  a.out = out;
+  a.lse = lse;
+  const size_t need = partial_bytes(num_rows, a.split_slots);
+  if (!partials || partials_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "partials buffer of %zu bytes needed, %zu given", need,
+                partials ? partials_bytes : (size_t)0);
+  if (!aligned(partials, 16)) return fail(DSA_ERR_INVALID_ARG, "partials must be 16-byte aligned");
+  partial_views(a, const_cast<void*>(partials), num_rows);
+  return hip_status(dsa::launch_mla_combine(a, static_cast<hipStream_t>(stream)),
+                    "dsa_lse_combine launch");
 }
 
 }  // extern "C"

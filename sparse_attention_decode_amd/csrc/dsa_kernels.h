@@ -63,21 +63,28 @@ struct MlaArgs {
   const uint16_t* q;  // [R][96][576] bf16
   const int32_t* idx; // [R][k]
   const int32_t* phys; // [R][k] pool rows of idx, or null
+  const int32_t* count; // [R] selected entries at the front of each idx row, or null (all k)
   int32_t k;
   float softmax_scale;
   float tensor_scale;  // NVFP4 latent tensor scale (1 for FP8)
   uint16_t* out;       // [R][96][512] bf16
   float* lse;          // [R][96] or null
-  uint16_t* part_o;    // [R][nsplit][12 waves][16][64 lanes][4] fp16 normalised split outputs
+  uint16_t* part_o;    // [R][split_slots][12 waves][16][64 lanes][4] fp16 normalised split outputs
                        // * 2^part_exp, in the attention kernel's accumulator layout
-  float* part_lse;     // [R][nsplit][96] base-2 log-sum-exp of each split
-  int32_t* part_exp;   // [R][nsplit][96] power-of-two scale exponent of each split output
-  int32_t nsplit;
+  float* part_lse;     // [R][split_slots][96] base-2 log-sum-exp of each split
+  int32_t* part_exp;   // [R][split_slots][96] power-of-two scale exponent of each split output
+  int32_t nsplit;           // splits of this call (grid y)
   int32_t tokens_per_split;
+  int32_t split_base;       // first partial slot of this call's splits in each row
+  int32_t split_slots;      // partial slots per row (nsplit, or shards x nsplit across shards)
+  int32_t out_direct;       // one split, no partials: the attention writes out and lse itself
 };
 int mla_num_splits(int32_t num_rows, int32_t k, bool invariant);
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant);
-hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s);
+// Attention (grid rows x nsplit), then, unless out_direct or !combine, the split combine.
+hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, bool combine, hipStream_t s);
+// The log-sum-exp combine of split_slots partial slots per row into out / lse.
+hipError_t launch_mla_combine(const MlaArgs& a, hipStream_t s);
 
 // The step before the path: quantise new tokens into their pool rows, and the indexer query.
 hipError_t launch_cache_write(const PoolView& pool, uint8_t* base, int ikey_fmt, int lat_fmt,
@@ -85,5 +92,14 @@ hipError_t launch_cache_write(const PoolView& pool, uint8_t* base, int ikey_fmt,
                               const uint16_t* ikey, const uint16_t* latent, hipStream_t s);
 hipError_t launch_quantize_query(int32_t num_rows, const uint16_t* q, const float* w, uint8_t* qo,
                                  float* wo, hipStream_t s);
+
+// Decode context parallelism emulated on one GPU: shard lists and the exact merge.
+size_t dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards);
+hipError_t launch_dcp_publish(int32_t R, int32_t k, int32_t W, int32_t shard, const float* scores,
+                              int64_t ld, const int32_t* idx, const int32_t* count, void* mb,
+                              hipStream_t s);
+hipError_t launch_dcp_merge(int32_t R, int32_t k, int32_t W, int32_t variant, void* mb,
+                            int32_t* idx, int32_t* count, int32_t* shard_idx,
+                            int32_t* shard_count, int32_t* stats, hipStream_t s);
 
 }  // namespace dsa

@@ -289,8 +289,15 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   const int32_t* idx = a.idx + (int64_t)row * a.k;
   const int32_t* prow = a.phys + (int64_t)row * a.k;
   const int nvis = a.batch.row_pos[row] + 1;  // selected indices outside [0, nvis) are ignored
-  const int j0 = split * a.tokens_per_split;
-  const int j1 = min(a.k, j0 + a.tokens_per_split);
+  // The split's slots of the selection: fixed ranges of tokens_per_split, or, when the row's
+  // count of selected entries is given, that many entries spread evenly over the splits.
+  int nsel = a.k, per = a.tokens_per_split;
+  if (a.count) {
+    nsel = min(a.k, max(0, a.count[row]));
+    per = max(kTile, ((nsel + a.nsplit - 1) / a.nsplit + kTile - 1) / kTile * kTile);
+  }
+  const int j0 = split * per;
+  const int j1 = max(j0, min(nsel, j0 + per));
   const int32_t* bt = nullptr;
   if (!PHYS) {  // sequence of the row, by one ballot per 64 sequences
     int seq = 0;
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 
   // lane holds O^T[256dh + 16mt + 4g + i][head]
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-  if (a.nsplit == 1) {
+  if (a.out_direct) {
     uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + kDvHalf * dh;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt) {
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     // latent scale), the scale's exponent, and the split's base-2 log-sum-exp.  The fp16 values
     // keep the accumulator layout (wave, mt, lane, 4 values), so every store is 512 contiguous
     // bytes.
-    const int64_t slot = ((int64_t)row * a.nsplit + split) * DSA_MLA_HEADS + head;
+    const int64_t slot = ((int64_t)row * a.split_slots + a.split_base + split) * DSA_MLA_HEADS + head;
     float amax = 0.f;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt)
@@ -524,7 +531,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     const int e = (amax > 0.f) ? 14 - ilogbf(amax) : 0;
     const float sc = inv * ldexpf(1.f, e);
     uint2* po = reinterpret_cast<uint2*>(a.part_o) +
-                (((int64_t)row * a.nsplit + split) * kWavesM + wave) * (kDvHalf / 16) * kWave + lane;
+                (((int64_t)row * a.split_slots + a.split_base + split) * kWavesM + wave) *
+                    (kDvHalf / 16) * kWave + lane;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt)
       po[mt * kWave] = uint2{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
@@ -550,9 +558,9 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int head = 16 * (wave >> 1) + (lane & 15);
   const int d = kDvHalf * (wave & 1) + 16 * mt + 4 * (lane >> 4);
-  const int64_t hbase = (int64_t)row * a.nsplit * DSA_MLA_HEADS + head;
+  const int64_t hbase = (int64_t)row * a.split_slots * DSA_MLA_HEADS + head;
   const uint2* pbase = reinterpret_cast<const uint2*>(a.part_o) +
-                       ((int64_t)row * a.nsplit * kWavesM + wave) * (kDvHalf / 16) * kWave +
+                       ((int64_t)row * a.split_slots * kWavesM + wave) * (kDvHalf / 16) * kWave +
                        mt * kWave + lane;
   const int64_t pstride = (int64_t)kWavesM * (kDvHalf / 16) * kWave;  // one split
   // One pass over groups of G splits: every load of a group (log-sum-exp, exponent and partial)
@@ -560,13 +568,13 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   // so up to G splits take one memory round trip.
   float M = -INFINITY, L = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.nsplit; s0 += G) {
+  for (int s0 = 0; s0 < a.split_slots; s0 += G) {
     float ls[G];
     int ex[G];
     uint2 v[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int sp = min(s0 + u, a.nsplit - 1);  // past the end: a repeat, weighted 0 below
+      const int sp = min(s0 + u, a.split_slots - 1);  // past the end: a repeat, weighted 0 below
       ls[u] = a.part_lse[hbase + (int64_t)sp * DSA_MLA_HEADS];
       ex[u] = a.part_exp[hbase + (int64_t)sp * DSA_MLA_HEADS];
       v[u] = pbase[(int64_t)sp * pstride];
@@ -574,7 +582,7 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
     float gm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      if (s0 + u < a.nsplit) gm = fmaxf(gm, ls[u]);
+      if (s0 + u < a.split_slots) gm = fmaxf(gm, ls[u]);
     const float m_new = fmaxf(M, gm);
     if (m_new == -INFINITY) continue;  // nothing attended so far
     const float r = exp2f(M - m_new);  // M = -inf: 0 (L and acc are 0 then)
@@ -584,7 +592,7 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
     M = m_new;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const float wgt = (s0 + u < a.nsplit && ls[u] != -INFINITY) ? exp2f(ls[u] - M) : 0.f;
+      const float wgt = (s0 + u < a.split_slots && ls[u] != -INFINITY) ? exp2f(ls[u] - M) : 0.f;
       L += wgt;
       const float w2 = ldexpf(wgt, -ex[u]);
       acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
@@ -628,7 +636,19 @@ size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant) {
   return (size_t)num_rows * ns * DSA_MLA_HEADS * (DSA_MLA_DV * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
-hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
+hipError_t launch_mla_combine(const MlaArgs& a, hipStream_t s) {
+  if (a.batch.num_rows <= 0) return hipSuccess;
+  const dim3 cgrid((unsigned)a.batch.num_rows, 2 * kWavesM);
+  if (a.split_slots <= 4)
+    hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
+  else if (a.split_slots <= 8)
+    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, bool combine, hipStream_t s) {
   if (a.batch.num_rows <= 0) return hipSuccess;
   dim3 grid((unsigned)a.batch.num_rows, (unsigned)a.nsplit);
   if (lat_fmt == DSA_LATENT_FP8)
@@ -641,15 +661,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int lat_fmt, hipStream_t s) {
   else
     hipLaunchKernelGGL((sparse_mla_kernel<DSA_LATENT_NVFP4, false>), grid, dim3(kThreadsM), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  const dim3 cgrid((unsigned)a.batch.num_rows, 2 * kWavesM);
-  if (a.nsplit <= 4)
-    hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
-  else if (a.nsplit <= 8)
-    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(512), 0, s, a);
-  return hipGetLastError();
+  if (e != hipSuccess || a.out_direct || !combine) return e;
+  return launch_mla_combine(a, s);
 }
 
 }  // namespace dsa

@@ -67,7 +67,7 @@ def lib():
         L.synth_qmla.argtypes = [u64, i64, i64, vp]
         L.synth_fill_pool.restype = None
         L.synth_fill_pool.argtypes = [u64, i32, i32, i32, i64, i64, i64, i64, i64, i64, vp, i32,
-                                      vp, i64, vp, vp]
+                                      vp, i64, vp, vp, i64, i64]
         _lib = L
     return _lib
 
@@ -166,6 +166,8 @@ class Workload:
     row_id: np.ndarray = None
     block_table: np.ndarray = field(default=None, repr=False)
     num_blocks: int = 0
+    tok_stride: int = 1   # token t of a pool sequence is generator token t * stride + offset
+    tok_offset: int = 0
 
     def __post_init__(self):
         self.seq_len = np.asarray(self.seq_len, np.int64)
@@ -213,6 +215,24 @@ def shuffled_block_table(seed: int, seq_len, block_size: int, spare: int):
     return bt, total
 
 
+def shard_workload(w: Workload, W: int, r: int) -> Workload:
+    """Shard r of W of workload w under token-interleaved sharding: token j of a shard sequence
+    is token j*W + r of the original sequence (same data), and a row at position p sees the
+    shard's tokens [0, (p - r) // W] (p >= r).  The shard's pool has its own shuffled block table;
+    the rows keep their generator ids, so their queries are those of w."""
+    assert w.tok_stride == 1 and w.tok_offset == 0 and 0 <= r < W
+    assert np.all(w.row_pos >= r), "every row must see at least one token of every shard"
+    lens = np.array([(int(L) - r + W - 1) // W for L in w.seq_len], np.int64)
+    bt, nb = shuffled_block_table(w.seed * 1000003 + 7919 * (r + 1) + W, lens, w.block_size,
+                                  w.spare_blocks)
+    return Workload(f"{w.name}-shard{r}of{W}", w.seed, lens, w.row_seq.copy(),
+                    (w.row_pos - r) // W, ikey_fmt=w.ikey_fmt, lat_fmt=w.lat_fmt,
+                    block_size=w.block_size, k=w.k, softmax_scale=w.softmax_scale,
+                    lat_tensor_scale=w.lat_tensor_scale, spare_blocks=w.spare_blocks, wq=w.wq,
+                    seq_id=w.seq_id.copy(), row_id=w.row_id.copy(), block_table=bt,
+                    num_blocks=nb, tok_stride=W, tok_offset=r)
+
+
 def fill_pool(w: Workload, layout) -> np.ndarray:
     """Pool bytes [num_blocks * row_bytes] for workload `w`.  `layout` gives row_bytes and the
     four in-row byte offsets (from the library's layout descriptor)."""
@@ -224,7 +244,8 @@ def fill_pool(w: Workload, layout) -> np.ndarray:
     lib().synth_fill_pool(w.seed, w.ikey_fmt, w.lat_fmt, w.block_size, row_bytes,
                           int(layout["latent_off"]), int(layout["latent_scale_off"]),
                           int(layout["ikey_off"]), int(layout["ikey_scale_off"]), w.num_blocks,
-                          _p(pool), w.num_seqs, _p(bt), bt.shape[1], _p(lens), _p(sid))
+                          _p(pool), w.num_seqs, _p(bt), bt.shape[1], _p(lens), _p(sid),
+                          w.tok_stride, w.tok_offset)
     return pool
 
 

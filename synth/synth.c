@@ -283,7 +283,7 @@ void synth_fill_pool(uint64_t seed, int ikey_fmt, int lat_fmt, int block_size, i
                      int64_t lat_off, int64_t lat_scale_off, int64_t ikey_off,
                      int64_t ikey_scale_off, int64_t num_blocks, uint8_t* pool, int num_seqs,
                      const int32_t* block_table, int64_t ld_bt, const int64_t* seq_len,
-                     const int64_t* seq_id) {
+                     const int64_t* seq_id, int64_t tok_stride, int64_t tok_offset) {
   const int bs = block_size;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < num_blocks; ++b) memset(pool + b * row_bytes, 0xFF, (size_t)row_bytes);
@@ -314,6 +314,35 @@ void synth_fill_pool(uint64_t seed, int ikey_fmt, int lat_fmt, int block_size, i
       int64_t phys = block_table[q * ld_bt + blk];
       uint8_t* row = pool + phys * row_bytes;
       int64_t sid = seq_id ? seq_id[q] : q;
+      if (tok_stride != 1 || tok_offset != 0) {
+        /* a token-interleaved shard: pool token t is generator token t * stride + offset */
+        for (int64_t i = 0; i < ntok; ++i) {
+          const int64_t g = (tok0 + i) * tok_stride + tok_offset;
+          if (lat_fmt == 0)
+            synth_latent_fp8(seed, sid, g, 1, lat + i * MLA_DQK, lat_scale + i);
+          else
+            synth_latent_nvfp4(seed, sid, g, 1, lat + i * 288, lat_nv_scale + i * 36);
+          if (ikey_fmt == 0)
+            synth_ikey_fp8(seed, sid, g, 1, key + i * IDX_DIM, key_scale + i);
+          else
+            synth_ikey_mxfp4(seed, sid, g, 1, key + i * 64, key_mx_scale + i * 4);
+        }
+        if (lat_fmt == 0) {
+          memcpy(row + lat_off, lat, (size_t)(ntok * MLA_DQK));
+          memcpy(row + lat_scale_off, lat_scale, (size_t)(ntok * 4));
+        } else {
+          memcpy(row + lat_off, lat, (size_t)(ntok * 288));
+          memcpy(row + lat_scale_off, lat_nv_scale, (size_t)(ntok * 36));
+        }
+        if (ikey_fmt == 0) {
+          memcpy(row + ikey_off, key, (size_t)(ntok * IDX_DIM));
+          memcpy(row + ikey_scale_off, key_scale, (size_t)(ntok * 4));
+        } else {
+          memcpy(row + ikey_off, key, (size_t)(ntok * 64));
+          memcpy(row + ikey_scale_off, key_mx_scale, (size_t)(ntok * 4));
+        }
+        continue;
+      }
       if (lat_fmt == 0) {
         synth_latent_fp8(seed, sid, tok0, ntok, lat, lat_scale);
         memcpy(row + lat_off, lat, (size_t)(ntok * MLA_DQK));

@@ -185,3 +185,45 @@ def test_front_entry_points_validate_before_launch():
     assert lib.dsa_quantize_query(2, ctypes.c_void_p(0x2002), p, p, p, None) == bad
     assert lib.dsa_quantize_query(2, p, p, ctypes.c_void_p(0x2001), p, None) == bad
     assert lib.dsa_quantize_query(0, None, None, None, None, None) == ok
+
+
+def test_dcp_entry_points_validate_before_launch():
+    # mailbox sizing, bad arguments and missing buffers are rejected before any launch
+    lib = L.lib()
+    p = ctypes.c_void_p(0x2000)
+    mb = ctypes.c_void_p(0x10000)
+    ok, bad, ws = L.DSA_OK, L.DSA_ERR_INVALID_ARG, L.DSA_ERR_WORKSPACE
+    need = lib.dsa_dcp_mailbox_bytes(16, 2048, 8)
+    assert need == (8 * 16 * 2048 * 8 + 8 * 16 * 4 + 15) // 16 * 16
+    assert lib.dsa_dcp_mailbox_bytes(16, 2049, 8) == 0 and lib.dsa_dcp_mailbox_bytes(16, 8, 9) == 0
+    assert lib.dsa_dcp_publish(16, 2048, 8, 0, p, 4096, p, p, mb, need - 1, None) == ws
+    assert lib.dsa_dcp_publish(16, 2048, 8, 8, p, 4096, p, p, mb, need, None) == bad
+    assert lib.dsa_dcp_publish(16, 2048, 8, -1, p, 4096, p, p, mb, need, None) == bad
+    assert lib.dsa_dcp_publish(16, 2048, 8, 0, None, 4096, p, p, mb, need, None) == bad
+    assert lib.dsa_dcp_publish(16, 2048, 8, 0, p, 4096, p, p, ctypes.c_void_p(0x10004), need,
+                               None) == bad
+    assert lib.dsa_dcp_publish(16, 0, 8, 0, p, 4096, p, p, mb, need, None) == bad
+    assert lib.dsa_dcp_publish(16, 2048, 0, 0, p, 4096, p, p, mb, need, None) == bad
+    assert lib.dsa_dcp_merge(16, 2048, 8, 3, mb, need, p, p, p, p, None, None) == bad
+    assert lib.dsa_dcp_merge(16, 2048, 8, 0, mb, need, p, p, None, p, None, None) == bad
+    assert lib.dsa_dcp_merge(16, 2048, 8, 0, None, 0, p, p, p, p, None, None) == ws
+    assert lib.dsa_dcp_merge(0, 2048, 8, 0, None, 0, None, None, None, None, None, None) == ok
+    pb = lib.dsa_dcp_partials_bytes(4, 2048, 2, 0)
+    # the shard split count is sized for k / shards = 1,024 tokens: at 4 rows, 32 splits per shard
+    assert pb == 4 * 2 * 32 * 96 * (512 * 2 + 8)
+    assert lib.dsa_dcp_partials_bytes(4, 2048, 9, 0) == 0
+    assert lib.dsa_lse_combine(4, 2048, 0, 0, mb, pb, p, None, None) == bad
+    assert lib.dsa_lse_combine(4, 2048, 2, 2, mb, pb, p, None, None) == bad
+    assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb - 1, p, None, None) == ws
+    assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb, ctypes.c_void_p(0x2008), None, None) == bad
+    assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb, None, None, None) == bad
+    assert lib.dsa_lse_combine(0, 2048, 2, 0, None, 0, None, None, None) == ok
+    kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
+    b = _fake_batch(num_rows=4)
+    pool = ctypes.c_void_p(0x100000)
+    assert lib.sparse_mla_decode_shard(ctypes.byref(kv), pool, ctypes.byref(b), p, p, None, None,
+                                       2048, 0.1, 2, 2, mb, pb, None) == bad
+    assert lib.sparse_mla_decode_shard(ctypes.byref(kv), pool, ctypes.byref(b), p, p, None, None,
+                                       2048, 0.1, 0, 2, mb, pb - 1, None) == ws
+    assert lib.sparse_mla_decode_shard(ctypes.byref(kv), pool, ctypes.byref(b), None, p, None,
+                                       None, 2048, 0.1, 0, 2, mb, pb, None) == bad
