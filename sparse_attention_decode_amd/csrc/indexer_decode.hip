@@ -64,27 +64,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, i
                                            0x00020000 /* gfx9: 32-bit data format */);
 }
 
+// AUX: the loads' cache policy, 0 or 2 (non-temporal: a key stream far larger than the
+// memory-side cache is read once per step, so its lines are not worth allocating).
+template <int AUX>
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, int off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX);
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
-template <int KFMT>
+template <int KFMT, int AUX>
 __device__ __forceinline__ void load_key_page(KeyFrag* f, __amdgpu_buffer_rsrc_t rs,
                                               const LaneOffsets& o) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     if (KFMT == DSA_IKEY_FP8) {
       const int k = o.key + nt * 16 * DSA_INDEX_DIM;
-      const uint4 lo = ld16(rs, k), hi = ld16(rs, k + 64);
+      const uint4 lo = ld16<AUX>(rs, k), hi = ld16<AUX>(rs, k + 64);
       f[nt].b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
                     (int)hi.w};
-      f[nt].scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.scale + nt * 64, 0, 0));
+      f[nt].scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.scale + nt * 64, 0, AUX));
       f[nt].escale = 127;
     } else {
-      const uint4 v = ld16(rs, o.key + nt * 16 * (DSA_INDEX_DIM / 2));
+      const uint4 v = ld16<AUX>(rs, o.key + nt * 16 * (DSA_INDEX_DIM / 2));
       f[nt].b = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      f[nt].escale = __builtin_amdgcn_raw_buffer_load_b8(rs, o.scale + nt * 64, 0, 0);
+      f[nt].escale = __builtin_amdgcn_raw_buffer_load_b8(rs, o.scale + nt * 64, 0, AUX);
       f[nt].scale = 1.0f;
     }
   }
@@ -97,9 +100,10 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, __amdgpu_buffer_rsrc_t
 // tile.  Scores stay in registers for G pages and then leave as coalesced 256-byte streaming
 // stores: for one or two rows G covers the whole run, so no store is pending while page loads are
 // (gfx9 counts loads and stores on one counter, and a mix makes every later wait a full drain).
-template <int R, int KFMT, bool HIST>
+template <int R, int KFMT, bool HIST, bool NT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_kernel(IndexerArgs a) {
+  constexpr int AUX = NT ? 2 : 0;  // cache policy of the key loads
   constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
@@ -171,7 +175,7 @@ void indexer_kernel(IndexerArgs a) {
   };
   const LaneOffsets lo = lane_offsets<KFMT>(a.pool, g, c);
   KeyFrag buf[2][4];
-  load_key_page<KFMT>(buf[0], page_rsrc(0), lo);
+  load_key_page<KFMT, AUX>(buf[0], page_rsrc(0), lo);
 
   // queries and weights to LDS (the first page is on its way meanwhile)
 #pragma unroll
@@ -196,7 +200,7 @@ void indexer_kernel(IndexerArgs a) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
-      load_key_page<KFMT>(buf[(u + 1) & 1], page_rsrc(i + 1), lo);  // always issued
+      load_key_page<KFMT, AUX>(buf[(u + 1) & 1], page_rsrc(i + 1), lo);  // always issued
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const int blk = page_of(i);
@@ -298,15 +302,19 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// nt: stream the keys past the caches (decode with a histogram only).
 template <int KFMT>
-hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s) {
+hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s,
+                            bool nt = false) {
   switch (rows) {
-#define DSA_CASE(R)                                                                            \
-  case R:                                                                                      \
-    if (a.hist)                                                                                \
-      hipLaunchKernelGGL((indexer_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);  \
-    else                                                                                       \
-      hipLaunchKernelGGL((indexer_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a); \
+#define DSA_CASE(R)                                                                              \
+  case R:                                                                                        \
+    if (a.hist && nt)                                                                            \
+      hipLaunchKernelGGL((indexer_kernel<R, KFMT, true, true>), grid, dim3(kThreads), 0, s, a); \
+    else if (a.hist)                                                                             \
+      hipLaunchKernelGGL((indexer_kernel<R, KFMT, true>), grid, dim3(kThreads), 0, s, a);       \
+    else                                                                                         \
+      hipLaunchKernelGGL((indexer_kernel<R, KFMT, false>), grid, dim3(kThreads), 0, s, a);      \
     break;
     DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
 #undef DSA_CASE
@@ -352,8 +360,14 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   a.pages_per_wave = (int32_t)ppw;
   const int64_t per_wg = ppw * kWaves;
   dim3 grid((unsigned)((nblk + per_wg - 1) / per_wg), (unsigned)a.batch.num_seqs);
-  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s)
-                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s);
+  // A key stream much larger than the 256 MB memory-side cache cannot stay there between steps:
+  // load it non-temporally, leaving the cache to the scores and latents the next kernels read.
+  // A small one (a short context) is re-read from that cache on the next step: keep it there.
+  const int64_t key_bytes = a.batch.num_seqs * max_context *
+                            (ikey_fmt == DSA_IKEY_FP8 ? DSA_INDEX_DIM + 4 : DSA_INDEX_DIM / 2 + 4);
+  const bool nt = key_bytes >= ((int64_t)64 << 20);
+  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s, nt)
+                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s, nt);
 }
 
 // Prefill: the rows of a sequence are cut into tiles of 16 (queries in LDS); each workgroup

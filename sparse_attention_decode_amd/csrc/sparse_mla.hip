@@ -109,12 +109,14 @@ __device__ __forceinline__ int opaque(int x) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
 }
+// The gathers are non-temporal: each selected latent is read once per step.
+#define DSA_GATHER_POLICY " nt"
 __device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" DSA_GATHER_POLICY
                :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" DSA_GATHER_POLICY
                :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
 }
 
@@ -228,6 +230,7 @@ __device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_
 }
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -535,8 +538,12 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
                     (kDvHalf / 16) * kWave + lane;
 #pragma unroll
     for (int mt = 0; mt < kDvHalf / 16; ++mt)
-      po[mt * kWave] = uint2{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
-                             f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
+      // streamed out (non-temporal): read once by the combine, they should not sit dirty in
+      // the memory-side cache and be written back while the next step's scorer streams keys
+      __builtin_nontemporal_store(
+          v2u{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
+              f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)},
+          reinterpret_cast<v2u*>(po + mt * kWave));
     if (g == 0 && dh == 0) {
       a.part_lse[slot] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
       a.part_exp[slot] = e;
