@@ -180,8 +180,11 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.part_exp = nullptr;
+  a.nt_partials = 0;
   if (!a.out_direct) {
     const size_t need = partial_bytes(batch->num_rows, a.split_slots);
+    // 16 MB and more: the set would evict as dirty lines during the next step's key stream
+    a.nt_partials = need >= ((size_t)16 << 20);
     if (!workspace || workspace_bytes < need)
       return fail(DSA_ERR_WORKSPACE, "%s of %zu bytes needed, %zu given",
                   shard >= 0 ? "partials buffer" : "workspace", need,

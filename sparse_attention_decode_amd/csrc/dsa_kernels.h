@@ -78,6 +78,7 @@ struct MlaArgs {
   int32_t split_base;       // first partial slot of this call's splits in each row
   int32_t split_slots;      // partial slots per row (nsplit, or shards x nsplit across shards)
   int32_t out_direct;       // one split, no partials: the attention writes out and lse itself
+  int32_t nt_partials;      // store the partials non-temporally (a large set)
 };
 int mla_num_splits(int32_t num_rows, int32_t k, bool invariant);
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant);

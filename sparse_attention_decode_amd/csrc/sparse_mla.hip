@@ -537,13 +537,17 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
                 (((int64_t)row * a.split_slots + a.split_base + split) * kWavesM + wave) *
                     (kDvHalf / 16) * kWave + lane;
 #pragma unroll
-    for (int mt = 0; mt < kDvHalf / 16; ++mt)
-      // streamed out (non-temporal): read once by the combine, they should not sit dirty in
-      // the memory-side cache and be written back while the next step's scorer streams keys
-      __builtin_nontemporal_store(
-          v2u{f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
-              f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)},
-          reinterpret_cast<v2u*>(po + mt * kWave));
+    for (int mt = 0; mt < kDvHalf / 16; ++mt) {
+      // Large partial sets are streamed out (non-temporal): read once by the combine, they
+      // should not sit dirty in the memory-side cache and be written back while the next step's
+      // scorer streams keys.  Small ones stay cached for the combine.
+      const v2u w = {f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
+                     f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
+      if (a.nt_partials)
+        __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(po + mt * kWave));
+      else
+        *reinterpret_cast<v2u*>(po + mt * kWave) = w;
+    }
     if (g == 0 && dh == 0) {
       a.part_lse[slot] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
       a.part_exp[slot] = e;
