@@ -49,6 +49,7 @@ struct TopkArgs {
   int32_t* phys;  // or null
   // workspace views (set by launch_topk)
   uint32_t* slice_cnt;  // [R][num_slices] survivors per slice
+  uint32_t* level1;     // [R][2] threshold bin of the top 11 key bits, and how many of k it holds
   uint2* cand;          // [R][cand_ld] survivors (order key, token index), slice-major
   int64_t cand_ld;
   int32_t num_slices;

@@ -627,6 +627,9 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
 
 }  // namespace
 
+#ifndef DSA_MLA_MAX_SPLITS
+#define DSA_MLA_MAX_SPLITS 32
+#endif
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
 #endif
@@ -637,6 +640,9 @@ int mla_num_splits(int32_t num_rows, int32_t k, bool invariant) {
   const int tiles = (k + kTile - 1) / kTile;
   int want = (DSA_MLA_TARGET_WGS + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
   if (want > tiles) want = tiles;
+  // at most 32 splits (64 tokens each at k = 2,048): below that size a split is one tile, and the
+  // combine's extra round over the slots costs more than the parallelism gains (one row: 1.4 us)
+  if (want > DSA_MLA_MAX_SPLITS) want = DSA_MLA_MAX_SPLITS;
   if (want < 1) want = 1;
   return want;
 }

@@ -170,10 +170,18 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a)
   for (int j = 0; j < kPerThread; ++j)
     if (mask & (1u << j)) out[pos++] = uint2{order_key(v[j]), (uint32_t)(base + kPerThread * tid + j)};
   if (tid == 0) a.slice_cnt[(int64_t)row * a.num_slices + slice] = total;
+  if (tid == 0 && slice == 0) {  // every slice found the same bin; the resolve starts from it
+    a.level1[2 * row] = b1;
+    a.level1[2 * row + 1] = rest;
+  }
 }
 
 // ------------------------------------------------------------------ resolve
+constexpr int kBtCache = 4096;  // block-table entries of a row cached in LDS (contexts to 256K)
+constexpr int kBtPer = kBtCache / kResolveThreads;
+
 struct ResolveShared {
+  int32_t bt[kBtCache];
   uint32_t hist[kBins];
   uint32_t key[kCap];
   int32_t idx[kCap];
@@ -203,12 +211,20 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     if (tid == 0) a.count[row] = n;
     return;
   }
-  const int nsl = (n + kTopkSlice - 1) / kTopkSlice;
-  // The histogram row is loaded now (it is independent of everything below) and returned to
-  // zero for the next call.
-  uint32_t hv[kBins / kResolveThreads];
+  // the row's block-table entries, for the pool rows of the selection at the end: loaded now
+  // into registers (their latency overlaps the loads below), moved to LDS before they are used
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const bool bt_cached = phys != nullptr && nblk <= kBtCache;
+  int32_t btv[kBtPer];
 #pragma unroll
-  for (int j = 0; j < kBins / kResolveThreads; ++j) hv[j] = hist_row[tid + kResolveThreads * j];
+  for (int j = 0; j < kBtPer; ++j) {
+    const int i = tid + kResolveThreads * j;
+    btv[j] = (bt_cached && i < nblk) ? bt[i] : 0;
+  }
+  const int nsl = (n + kTopkSlice - 1) / kTopkSlice;
+  // level 1 (the top 11 key bits) was resolved by the filter from the histogram
+  const uint32_t b1 = a.level1[2 * row];
+  uint32_t need = a.level1[2 * row + 1];
 
   // survivors per slice -> exclusive prefix
   {
@@ -258,15 +274,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
   auto key_of = [&](uint32_t e) -> uint32_t { return in_lds ? sh.key[e] : cand_at(e).x; };
   auto tok_of = [&](uint32_t e) -> int32_t { return in_lds ? sh.idx[e] : (int32_t)cand_at(e).y; };
 
-  // level 1 from the histogram, which is then returned to zero for the next call
+  // the histogram is consumed: return it to zero for the next call
 #pragma unroll
-  for (int j = 0; j < kBins / kResolveThreads; ++j) {
-    sh.hist[tid + kResolveThreads * j] = hv[j];
-    hist_row[tid + kResolveThreads * j] = 0;
-  }
-  __syncthreads();
-  uint32_t need;
-  const uint32_t b1 = select_bin<kResolveThreads>(sh.hist, kBins, (uint32_t)k, &need, sh.sc, sh.wtot);
+  for (int j = 0; j < kBins / kResolveThreads; ++j) hist_row[tid + kResolveThreads * j] = 0;
 
   // levels 2 and 3: key bits [20:10] and [9:0] among survivors sharing the chosen prefix
   uint32_t prefix = b1 << 21, mask = 0xFFE00000u;
@@ -290,6 +300,17 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
   }
   const uint32_t T = prefix;  // exact key of the k-th largest score
   const uint32_t E = need;    // keys equal to T that make the cut (the lowest-index ones)
+  if (bt_cached) {
+#pragma unroll
+    for (int j = 0; j < kBtPer; ++j) {
+      const int i = tid + kResolveThreads * j;
+      if (i < nblk) sh.bt[i] = btv[j];
+    }
+    __syncthreads();
+  }
+  auto phys_sel = [&](int s) {
+    return (bt_cached ? sh.bt[s / kBlock] : bt[s / kBlock]) * kBlock + (s % kBlock);
+  };
 
   // ordered selection over the survivors (token order)
   uint32_t gt_run = 0, eq_run = 0;
@@ -323,7 +344,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
       if (slot < (uint32_t)k) {
         const int32_t s = tok_of(e0 + j);
         out[slot] = s;
-        if (phys) phys[slot] = phys_of(s);
+        if (phys) phys[slot] = phys_sel(s);
       }
     }
     gt_run += total & 0xFFFFu;
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
 
 size_t topk_workspace_bytes(int32_t num_rows, int64_t max_context) {
   const int64_t ns = (max_context + kTopkSlice - 1) / kTopkSlice;
-  return (size_t)num_rows * (kBins + ns + 2 * ns * kTopkSlice + 2) * sizeof(uint32_t);
+  return (size_t)num_rows * (kBins + ns + 2 + 2 * ns * kTopkSlice + 2) * sizeof(uint32_t);
 }
 
 hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStream_t s) {
@@ -349,7 +370,8 @@ hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStr
   uint32_t* w = static_cast<uint32_t*>(ws);
   uint32_t* hist_ws = w;
   a.slice_cnt = w + R * kBins;
-  uint32_t* cand = a.slice_cnt + R * a.num_slices;
+  a.level1 = a.slice_cnt + R * a.num_slices;
+  uint32_t* cand = a.level1 + 2 * R;
   cand += ((uintptr_t)cand & 7) ? 1 : 0;  // 8-byte alignment of the (key, index) pairs
   a.cand = reinterpret_cast<uint2*>(cand);
   a.vec_ok = ((a.ld & 3) == 0) && ((((uintptr_t)a.scores) & 15) == 0);

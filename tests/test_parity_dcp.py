@@ -102,11 +102,18 @@ def test_merge_matches_oracle_protocol(W, k):
                 assert np.array_equal(gs[r, i, :len(loc)], loc) and np.all(gs[r, i, len(loc):] == -1)
 
 
-@pytest.mark.parametrize("W,variant", [(4, sad.MERGE_PACKED), (3, sad.MERGE_SCORES)])
-def test_sharded_decode_step(W, variant):
-    print(f"\n[case] dcp decode step W={W} variant={variant}", flush=True)
-    wl = synth.Workload("dcp-step", 31, [40000, 9000, 26000], [0, 1, 1, 2],
-                        [39999, 8990, 8999, 25999])
+@pytest.mark.parametrize("W,variant,lowp", [(4, sad.MERGE_PACKED, False),
+                                             (3, sad.MERGE_SCORES, False),
+                                             (8, sad.MERGE_GENERIC, True)])
+def test_sharded_decode_step(W, variant, lowp):
+    print(f"\n[case] dcp decode step W={W} variant={variant} lowp={lowp}", flush=True)
+    if lowp:  # MXFP4 keys, NVFP4 latents, a small k
+        wl = synth.Workload("dcp-step-lowp", 37, [30000, 5000], [0, 0, 1], [29990, 29999, 4999],
+                            ikey_fmt=sad.IKEY_MXFP4, lat_fmt=sad.LATENT_NVFP4,
+                            lat_tensor_scale=0.5, k=100)
+    else:
+        wl = synth.Workload("dcp-step", 31, [40000, 9000, 26000], [0, 1, 1, 2],
+                            [39999, 8990, 8999, 25999])
     k, R = wl.k, wl.num_rows
     full, _, _ = run_gpu(wl)
     ref_idx = full.idx.cpu().numpy()
