@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0
 
 
 def algorithmic_bytes(wl):
-    """Bytes the method must move per step (byte model): keys of every visible
+    """Bytes the method must move per step: keys of every visible
     token once per sequence, latents (+scales) of the selected tokens, the queries, the output
     and its log-sum-exp, and the block table.  Returns (total, indexer share)."""
     import numpy as np
@@ -296,8 +296,9 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_per_copy": 1 << 30, "copies": 3}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "design is described in DESIGN.md and not run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs "
+              "on a single GPU; sharding across GPUs is a design, not a measured path (the "
+              "cross-shard merge itself is measured on one GPU with --dcp W).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -5,13 +5,13 @@ TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_ba
 import this module.  It shares no code with the GPU path.  Plain numpy, small inputs.
 
 Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Long context: decode context
-parallelism with a sparse indexer (shard r of W holds every W-th token; partial attention outputs
-are merged by their log-sum-exp), §An exact top-k merge with 10x less traffic (each shard sends
-its best 1.5 k / W candidates packed with their score into 32 bits, every shard selects the same
-global top-k from the gathered candidates, and a shard that holds more of the top-k than it sent
-resends its full local top-k for that row; the generic merge sends every local top-k as fp32
-score and id pairs), and §AMD / Communication: Efficient cross-GPU communication (scores only are
-exchanged, ids stay local; a shared threshold and a consistent tie rule decide).
+parallelism with a sparse indexer (token-interleaved shards; the shards' partial attention
+results are merged by log-sum-exp), §An exact top-k merge with 10x less traffic (a message of
+1.5 k / W candidates per shard, each a 32-bit word carrying score and identity; the same global
+select on every shard; a resend of the whole local top-k by a shard whose share of the global
+top-k may exceed what it sent; as the baseline, whole local top-k lists of fp32 scores with
+indices), and §AMD / Communication: Efficient cross-GPU communication (a message of scores alone,
+token indices kept on their shard, ties settled by one rule applied everywhere).
 
 The merge reaches exactly the plain top-k of the whole sequence (score descending, token index
 ascending), so its result is pinned to oracle.topk; what this module adds is the protocol itself

@@ -43,9 +43,10 @@ def test_merge_equals_global_topk_random(variant):
 
 def test_resend_hand_worked():
     # W = 2, k = 4, C = ceil(1.5 * 4 / 2) = 3.  Shard 0 (tokens 0, 2, ..., 8) scores 9..5, shard 1
-    # (tokens 1, 3, ..., 9) scores .1...5.  Round 1: shard 0 sends 9, 8, 7, shard 1 sends .5, .4,
-    # .3; the 4th largest is .5 and shard 0's weakest sent (7) reaches it, so shard 0 resends its
-    # full local top-4; round 2 selects tokens 0, 2, 4, 6.  Bytes: 6 words + 4 resent words.
+    # (tokens 1, 3, ..., 9) scores .1...5.  First exchange: shard 0 sends 9, 8, 7, shard 1 sends
+    # .5, .4, .3; the 4th largest is .5 and shard 0's weakest sent (7) reaches it, so shard 0
+    # resends its full local top-4; the second select takes tokens 0, 2, 4, 6.  Bytes: 6 words +
+    # 4 resent words.
     s = np.zeros(10, np.float32)
     s[0::2] = [9, 8, 7, 6, 5]
     s[1::2] = [.1, .2, .3, .4, .5]
