@@ -350,7 +350,10 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   // group, at most 64).
   constexpr int kWaves = kThreads / kWave;
   const bool small = rows_per_seq <= 2;
-  const int64_t target = small ? 1024 : 2048;
+#ifndef DSA_IDX_TARGET_MANY
+#define DSA_IDX_TARGET_MANY 2048
+#endif
+  const int64_t target = small ? 1024 : DSA_IDX_TARGET_MANY;
   const int64_t cap = small ? kMaxPagesSmallR : kMaxPagesPerWave;
   const int64_t want = (nblk * a.batch.num_seqs + target - 1) / target;
   int64_t ppw = (want + kWaves - 1) / kWaves;
