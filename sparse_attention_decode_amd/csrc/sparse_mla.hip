@@ -110,6 +110,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
 }
 // The gathers are non-temporal: each selected latent is read once per step.
+// m0 carries the LDS address of each copy.  The compiler does not otherwise use m0 in these
+// kernels (their ISA has no m0 access but these writes), so setting it here disturbs nothing; it
+// is listed as clobbered, which the compiler notes it cannot promise to honour for m0.
 #define DSA_GATHER_POLICY " nt"
 __device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" DSA_GATHER_POLICY
