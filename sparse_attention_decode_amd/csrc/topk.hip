@@ -98,25 +98,39 @@ __device__ uint32_t select_bin(const uint32_t* hist, int nbins, uint32_t need, u
 }
 
 // ------------------------------------------------------------------ histogram (optional pass)
+// One histogram copy per wave: a row's scores crowd into few bins, and four waves adding to one
+// copy serialise on the same LDS words.
 __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t* hist) {
-  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t h[4][kBins];
   const int row = blockIdx.y;
   const int n = a.batch.row_pos[row] + 1;
   if (n <= a.k) return;
   const int s0 = blockIdx.x * kHistChunk;
   if (s0 >= n) return;
   const int s1 = min(n, s0 + kHistChunk);
-  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * kBins; i += 256) (&h[0][0])[i] = 0;
   __syncthreads();
   const float* sc = a.scores + (int64_t)row * a.ld;
+  uint32_t* hw = h[wave];
   for (int s = s0 + threadIdx.x * 4; s < s1; s += 256 * 4) {
+    if (a.vec_ok && s + 3 < s1) {
+      const float4 f = *reinterpret_cast<const float4*>(sc + s);
+      atomicAdd(&hw[order_key(f.x) >> 21], 1u);
+      atomicAdd(&hw[order_key(f.y) >> 21], 1u);
+      atomicAdd(&hw[order_key(f.z) >> 21], 1u);
+      atomicAdd(&hw[order_key(f.w) >> 21], 1u);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (s + j < s1) atomicAdd(&h[order_key(sc[s + j]) >> 21], 1u);
+      for (int j = 0; j < 4; ++j)
+        if (s + j < s1) atomicAdd(&hw[order_key(sc[s + j]) >> 21], 1u);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += 256)
-    if (h[i]) atomicAdd(&hist[(int64_t)row * kBins + i], h[i]);
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    const uint32_t v = h[0][i] + h[1][i] + h[2][i] + h[3][i];
+    if (v) atomicAdd(&hist[(int64_t)row * kBins + i], v);
+  }
 }
 
 // ------------------------------------------------------------------ filter
