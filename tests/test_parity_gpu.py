@@ -105,3 +105,23 @@ def test_prefill_attention_matches_decode_attention():
     assert bool(((ao - bo).abs() <= 2 * (2e-3 + 2e-2 * bo.abs())).all())
     check_workload(wl, a)
     check_workload(wl, b)
+
+
+@pytest.mark.parametrize("k", [1, 7])
+def test_decode_small_k(k):
+    # the smallest selections: k = 1 (the single best token; ties to the lowest index) and an odd
+    # k, over the ragged lengths (a row at position 0 sees one token)
+    print(f"\n[case] small k={k}", flush=True)
+    wl = _one_row_per_seq(f"smallk{k}", 49 + k, RAGGED, k=k)
+    layer, _, _ = run_gpu(wl)
+    check_workload(wl, layer)
+
+
+def test_prefill_first_chunk_from_position_zero():
+    # the first chunk of a prompt: rows 0..47 of one sequence, so the early rows see fewer
+    # tokens than k and row 0 sees only itself
+    print("\n[case] prefill from position 0", flush=True)
+    wl = synth.Workload("prefill0", 51, [48], [0] * 48, list(range(48)), k=16)
+    layer, _, _ = run_gpu(wl)
+    assert layer.prefill
+    check_workload(wl, layer)
