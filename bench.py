@@ -131,9 +131,10 @@ def cpu_baseline(cfg: int, wl, budget_s: float = 15.0):
 
 def time_front(wl, d, kv, steps: int):
     """Event time of the step before the path for one batch: every row's own new token quantised
-    into its pool row (index key and latent, dsa_cache_append) and the rows' indexer queries
-    quantised with the scale folded into the head weights (dsa_quantize_query).  Inputs are seeded
-    N(0, 1) bf16 values already on the device."""
+    into its pool row and the rows' indexer queries quantised with the scale folded into the head
+    weights.  The index keys and the queries go in one launch (dsa_indexer_front), the latents in
+    a second (dsa_cache_append with latents only).  Inputs are seeded N(0, 1) bf16 values already
+    on the device."""
     import torch
     import sparse_attention_decode_amd as sad
     R = wl.num_rows
@@ -150,8 +151,8 @@ def time_front(wl, d, kv, steps: int):
     stream = torch.cuda.current_stream()
 
     def run():
-        sad.dsa_cache_append(kv, d["pool"], d_slot, index_key=ikey, latent=lat)
-        sad.dsa_quantize_query(q, w, q_idx, w_out)
+        sad.dsa_indexer_front(kv, d["pool"], d_slot, ikey, q, w, q_idx, w_out)
+        sad.dsa_cache_append(kv, d["pool"], d_slot, latent=lat)
 
     for _ in range(5):
         run()
@@ -166,7 +167,7 @@ def time_front(wl, d, kv, steps: int):
     key_b = 132 if wl.ikey_fmt == 0 else 68
     lat_b = 580 if wl.lat_fmt == 0 else 324
     nbytes = R * (8 + 2 * 128 + 2 * 576 + key_b + lat_b) + R * 32 * (2 * 128 + 4 + 128 + 4)
-    return {"entry_points": "dsa_cache_append + dsa_quantize_query", "new_tokens": R,
+    return {"entry_points": "dsa_indexer_front + dsa_cache_append(latents)", "new_tokens": R,
             "query_rows": R, "us_per_step": us, "algorithmic_bytes_per_step": nbytes,
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9}
 

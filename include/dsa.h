@@ -243,6 +243,22 @@ DSA_API dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const
                                       uint8_t* q_idx, float* w_out, void* stream);
 
 /*
+ * dsa_indexer_front — what the scorer needs before it runs, in one launch: the new tokens' index
+ * keys into their pool rows, as dsa_cache_append with latent = NULL, and the indexer query, as
+ * dsa_quantize_query.  The results are bit-identical to those two calls.  The latents are left to
+ * a dsa_cache_append(index_key = NULL) call, which can run on another stream while the scorer
+ * runs, since the scorer reads no latent.
+ *   slot, index_key  as in dsa_cache_append (may be NULL when num_tokens is 0)
+ *   q, w, q_idx, w_out  as in dsa_quantize_query (may be NULL when num_rows is 0; w_out may be w)
+ * Returns INVALID_ARG for a bad layout, a negative count, a missing pointer or a misalignment
+ * (the alignments of the two calls); OK without a launch when both counts are 0.
+ */
+DSA_API dsa_status dsa_indexer_front(const dsa_kv_layout* kv, void* pool, int32_t num_tokens,
+                                     const int64_t* slot, const uint16_t* index_key,
+                                     int32_t num_rows, const uint16_t* q, const float* w,
+                                     uint8_t* q_idx, float* w_out, void* stream);
+
+/*
  * Decode context parallelism, emulated on one GPU ("vLLM Delivers Day-0 Support for Kimi K3.1
  * Pro", §Long context: decode context parallelism with a sparse indexer; §An exact top-k merge with
  * 10x less traffic; §AMD / Communication: Efficient cross-GPU communication).  Shard r of W holds

@@ -10,7 +10,8 @@ from ._lib import (DSAError, DeviceBatch, KVLayout, kv_layout, dsa_indexer_score
                    sparse_mla_decode, sparse_mla_prefill, sparse_mla_workspace_bytes, lib,
                    IKEY_FP8, IKEY_MXFP4, LATENT_FP8, LATENT_NVFP4, MAX_TOPK, HIST_BINS,
                    MAX_ROWS_PER_SEQ, INDEX_HEADS, INDEX_DIM, MLA_HEADS, MLA_DQK, MLA_DV, EXPORTS,
-                   BATCH_INVARIANT, dsa_cache_append, dsa_quantize_query, dsa_dcp_mailbox_bytes,
+                   BATCH_INVARIANT, dsa_cache_append, dsa_quantize_query, dsa_indexer_front,
+                   dsa_dcp_mailbox_bytes,
                    dsa_dcp_publish, dsa_dcp_merge, dsa_lse_combine, dsa_dcp_partials_bytes,
                    sparse_mla_decode_shard, MERGE_PACKED, MERGE_SCORES,
                    MERGE_GENERIC, MAX_SHARDS)
@@ -19,6 +20,7 @@ from .layer import DSALayer
 __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_bytes",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_workspace_bytes", "lib",
            "DSALayer", "EXPORTS", "BATCH_INVARIANT", "dsa_cache_append", "dsa_quantize_query",
+           "dsa_indexer_front",
            "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_lse_combine",
            "dsa_dcp_partials_bytes", "sparse_mla_decode_shard",
            "MERGE_PACKED", "MERGE_SCORES", "MERGE_GENERIC", "MAX_SHARDS"]

@@ -19,6 +19,7 @@ MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
            "sparse_mla_workspace_bytes",
            "sparse_mla_decode", "sparse_mla_prefill", "dsa_cache_append", "dsa_quantize_query",
+           "dsa_indexer_front",
            "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_dcp_partials_bytes",
            "sparse_mla_decode_shard", "dsa_lse_combine", "dsa_status_string", "dsa_last_error")
 MERGE_PACKED, MERGE_SCORES, MERGE_GENERIC, MAX_SHARDS = 0, 1, 2, 8
@@ -85,6 +86,9 @@ def lib():
         L.dsa_cache_append.argtypes = [ctypes.POINTER(KVLayout), vp, i32, vp, vp, vp, vp]
         L.dsa_quantize_query.restype = i32
         L.dsa_quantize_query.argtypes = [i32, vp, vp, vp, vp, vp]
+        L.dsa_indexer_front.restype = i32
+        L.dsa_indexer_front.argtypes = [ctypes.POINTER(KVLayout), vp, i32, vp, vp, i32, vp, vp, vp,
+                                        vp, vp]
         sz = ctypes.c_size_t
         L.dsa_dcp_mailbox_bytes.restype = sz
         L.dsa_dcp_mailbox_bytes.argtypes = [i32, i32, i32]
@@ -208,6 +212,18 @@ def dsa_quantize_query(q, w, q_idx, w_out, stream=None):
     (w_out may be w)."""
     _check(lib().dsa_quantize_query(q.shape[0], _ptr(q), _ptr(w), _ptr(q_idx), _ptr(w_out),
                                     _stream(stream)), "dsa_quantize_query")
+
+
+def dsa_indexer_front(kv: KVLayout, pool, slot, index_key, q, w, q_idx, w_out, stream=None):
+    """One launch of dsa_cache_append(index keys only) and dsa_quantize_query.  slot: int64 [n];
+    index_key: bf16 [n, 128]; q: bf16 [R, 32, 128]; w: f32 [R, 32]; q_idx: uint8 [R, 32, 128];
+    w_out: f32 [R, 32] (may be w).  slot/index_key may be None with n = 0, the query tensors
+    None with R = 0."""
+    n = 0 if slot is None else slot.numel()
+    R = 0 if q is None else q.shape[0]
+    _check(lib().dsa_indexer_front(ctypes.byref(kv), _ptr(pool), n, _ptr(slot), _ptr(index_key),
+                                   R, _ptr(q), _ptr(w), _ptr(q_idx), _ptr(w_out),
+                                   _stream(stream)), "dsa_indexer_front")
 
 
 def dsa_dcp_mailbox_bytes(num_rows: int, k: int, num_shards: int) -> int:

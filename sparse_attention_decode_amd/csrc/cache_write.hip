@@ -78,6 +78,29 @@ struct CacheWriteArgs {
   int32_t n;
 };
 
+// Token t's index key into its row (one wave; lane l holds elements 2l, 2l+1).
+template <int IKFMT>
+__device__ __forceinline__ void write_index_key(const CacheWriteArgs& a, int t, int lane,
+                                                uint8_t* row, int64_t s) {
+  const uint32_t p = reinterpret_cast<const uint32_t*>(a.ikey + (size_t)t * DSA_INDEX_DIM)[lane];
+  const float x0 = bf16_lo(p), x1 = bf16_hi(p);
+  if (IKFMT == DSA_IKEY_FP8) {
+    const float sc = fp8_token_scale(group_max<64>(fmaxf(fabsf(x0), fabsf(x1))));
+    const uint32_t c = enc_e4m3(x0 / sc) | (enc_e4m3(x1 / sc) << 8);
+    reinterpret_cast<uint16_t*>(row + a.ikey_off + s * DSA_INDEX_DIM)[lane] = (uint16_t)c;
+    if (lane == 0) reinterpret_cast<float*>(row + a.ikey_scale_off)[s] = sc;
+  } else {
+    // OCP MX block of 32 = 16 lanes: E8M0 exponent floor(log2 amax) - 2 (E2M1's top exponent)
+    const float amax = group_max<16>(fmaxf(fabsf(x0), fabsf(x1)));
+    int e = 127;
+    if (amax > 0.0f) e = min(max(__builtin_amdgcn_frexp_expf(amax) - 1 - 2 + 127, 0), 254);
+    const float X = __builtin_amdgcn_ldexpf(1.0f, e - 127);
+    const uint32_t c = enc_e2m1(x0 / X) | (enc_e2m1(x1 / X) << 4);
+    (row + a.ikey_off + s * (DSA_INDEX_DIM / 2))[lane] = (uint8_t)c;
+    if ((lane & 15) == 0) (row + a.ikey_scale_off + s * 4)[lane >> 4] = (uint8_t)e;
+  }
+}
+
 // One wave per token.  Index key: lane l holds elements 2l, 2l+1.  Latent: 144 chunks of four
 // elements; lane l holds chunks l, l + 64 and (lanes 0..15) l + 128, so an NVFP4 block of 16 is
 // four consecutive lanes.
@@ -91,25 +114,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   uint8_t* row = a.base + (slot >> 6) * a.row_bytes;
   const int64_t s = slot & 63;
 
-  if (a.ikey) {
-    const uint32_t p = reinterpret_cast<const uint32_t*>(a.ikey + (size_t)t * DSA_INDEX_DIM)[lane];
-    const float x0 = bf16_lo(p), x1 = bf16_hi(p);
-    if (IKFMT == DSA_IKEY_FP8) {
-      const float sc = fp8_token_scale(group_max<64>(fmaxf(fabsf(x0), fabsf(x1))));
-      const uint32_t c = enc_e4m3(x0 / sc) | (enc_e4m3(x1 / sc) << 8);
-      reinterpret_cast<uint16_t*>(row + a.ikey_off + s * DSA_INDEX_DIM)[lane] = (uint16_t)c;
-      if (lane == 0) reinterpret_cast<float*>(row + a.ikey_scale_off)[s] = sc;
-    } else {
-      // OCP MX block of 32 = 16 lanes: E8M0 exponent floor(log2 amax) - 2 (E2M1's top exponent)
-      const float amax = group_max<16>(fmaxf(fabsf(x0), fabsf(x1)));
-      int e = 127;
-      if (amax > 0.0f) e = min(max(__builtin_amdgcn_frexp_expf(amax) - 1 - 2 + 127, 0), 254);
-      const float X = __builtin_amdgcn_ldexpf(1.0f, e - 127);
-      const uint32_t c = enc_e2m1(x0 / X) | (enc_e2m1(x1 / X) << 4);
-      (row + a.ikey_off + s * (DSA_INDEX_DIM / 2))[lane] = (uint8_t)c;
-      if ((lane & 15) == 0) (row + a.ikey_scale_off + s * 4)[lane >> 4] = (uint8_t)e;
-    }
-  }
+  if (a.ikey) write_index_key<IKFMT>(a, t, lane, row, s);
 
   if (a.latent) {
     const uint2* src = reinterpret_cast<const uint2*>(a.latent + (size_t)t * DSA_MLA_DQK);
@@ -156,13 +161,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   }
 }
 
-// One wave per (row, head): 128 elements, two per lane.
-__global__ __launch_bounds__(256) void quantize_query_kernel(const uint16_t* __restrict__ q,
-                                                             const float* w, uint8_t* __restrict__ qo,
-                                                             float* wo, int32_t heads_total) {
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (h >= heads_total) return;
+// Query head h (one wave): 128 elements, two per lane.
+__device__ __forceinline__ void quantize_query_head(const uint16_t* __restrict__ q, const float* w,
+                                                    uint8_t* __restrict__ qo, float* wo, int h,
+                                                    int lane) {
   const uint32_t p = reinterpret_cast<const uint32_t*>(q + (size_t)h * DSA_INDEX_DIM)[lane];
   const float x0 = bf16_lo(p), x1 = bf16_hi(p);
   const float sc = fp8_token_scale(group_max<64>(fmaxf(fabsf(x0), fabsf(x1))));
@@ -170,6 +172,37 @@ __global__ __launch_bounds__(256) void quantize_query_kernel(const uint16_t* __r
       (uint16_t)(enc_e4m3(x0 / sc) | (enc_e4m3(x1 / sc) << 8));
   const float wh = w[h];
   if (lane == 0) wo[h] = wh * sc;
+}
+
+__global__ __launch_bounds__(256) void quantize_query_kernel(const uint16_t* __restrict__ q,
+                                                             const float* w, uint8_t* __restrict__ qo,
+                                                             float* wo, int32_t heads_total) {
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (h >= heads_total) return;
+  quantize_query_head(q, w, qo, wo, h, threadIdx.x & 63);
+}
+
+// The indexer front in one launch: workgroups [0, key_blocks) write the new tokens' index keys
+// (four tokens each), the rest quantise the query heads (four heads each).  The two halves touch
+// disjoint memory, so the split is only a partition of the grid.
+template <int IKFMT>
+__global__ __launch_bounds__(256) void indexer_front_kernel(CacheWriteArgs a, int32_t key_blocks,
+                                                            const uint16_t* __restrict__ q,
+                                                            const float* w, uint8_t* __restrict__ qo,
+                                                            float* wo, int32_t heads_total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < key_blocks) {
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= a.n) return;
+    const int64_t slot = a.slot[t];
+    if (slot < 0 || slot >= a.tokens) return;
+    write_index_key<IKFMT>(a, t, lane, a.base + (slot >> 6) * a.row_bytes, slot & 63);
+  } else {
+    const int h = (blockIdx.x - key_blocks) * 4 + wave;
+    if (h >= heads_total) return;
+    quantize_query_head(q, w, qo, wo, h, lane);
+  }
 }
 
 }  // namespace
@@ -206,6 +239,30 @@ hipError_t launch_quantize_query(int32_t num_rows, const uint16_t* q, const floa
                                  float* wo, hipStream_t st) {
   const int32_t heads = num_rows * DSA_INDEX_HEADS;
   quantize_query_kernel<<<dim3((heads + 3) / 4), dim3(256), 0, st>>>(q, w, qo, wo, heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_front(const PoolView& pool, uint8_t* base, int ikey_fmt, int32_t n,
+                                const int64_t* slot, const uint16_t* ikey, int32_t num_rows,
+                                const uint16_t* q, const float* w, uint8_t* qo, float* wo,
+                                hipStream_t st) {
+  CacheWriteArgs a{};
+  a.base = base;
+  a.row_bytes = pool.row_bytes;
+  a.ikey_off = pool.ikey_off;
+  a.ikey_scale_off = pool.ikey_scale_off;
+  a.tokens = pool.tokens;
+  a.slot = slot;
+  a.ikey = ikey;
+  a.n = n;
+  const int32_t key_blocks = (n + 3) / 4;
+  const int32_t heads = num_rows * DSA_INDEX_HEADS;
+  const dim3 grid(key_blocks + (heads + 3) / 4), block(256);
+  if (ikey_fmt == DSA_IKEY_FP8)
+    indexer_front_kernel<DSA_IKEY_FP8><<<grid, block, 0, st>>>(a, key_blocks, q, w, qo, wo, heads);
+  else
+    indexer_front_kernel<DSA_IKEY_MXFP4><<<grid, block, 0, st>>>(a, key_blocks, q, w, qo, wo,
+                                                                  heads);
   return hipGetLastError();
 }
 

@@ -385,6 +385,33 @@ dsa_status dsa_quantize_query(int32_t num_rows, const uint16_t* q, const float* 
                     "dsa_quantize_query launch");
 }
 
+dsa_status dsa_indexer_front(const dsa_kv_layout* kv, void* pool, int32_t num_tokens,
+                             const int64_t* slot, const uint16_t* index_key, int32_t num_rows,
+                             const uint16_t* q, const float* w, uint8_t* q_idx, float* w_out,
+                             void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_layout(kv, pool);
+  if (st != DSA_OK) return st;
+  if (num_tokens < 0 || num_rows < 0)
+    return fail(DSA_ERR_INVALID_ARG, "num_tokens and num_rows must be >= 0");
+  if (num_rows > (1 << 25)) return fail(DSA_ERR_INVALID_ARG, "num_rows too large");
+  if (num_tokens > 0 && (!slot || !index_key))
+    return fail(DSA_ERR_INVALID_ARG, "slot and index_key must be non-NULL when num_tokens > 0");
+  if (num_rows > 0 && (!q || !w || !q_idx || !w_out))
+    return fail(DSA_ERR_INVALID_ARG, "q, w, q_idx and w_out must be non-NULL when num_rows > 0");
+  if (num_tokens > 0 && (!aligned(slot, 8) || !aligned(index_key, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "slot must be 8-byte and index_key 4-byte aligned");
+  if (num_rows > 0 &&
+      (!aligned(q, 4) || !aligned(w, 4) || !aligned(q_idx, 2) || !aligned(w_out, 4)))
+    return fail(DSA_ERR_INVALID_ARG, "q, w, w_out must be 4-byte and q_idx 2-byte aligned");
+  if (num_tokens == 0 && num_rows == 0) return DSA_OK;
+  return hip_status(dsa::launch_indexer_front(pool_view(kv, pool), static_cast<uint8_t*>(pool),
+                                              kv->ikey_format, num_tokens, slot, index_key,
+                                              num_rows, q, w, q_idx, w_out,
+                                              static_cast<hipStream_t>(stream)),
+                    "dsa_indexer_front launch");
+}
+
 size_t dsa_dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards) {
   if (num_rows <= 0 || k < 1 || k > DSA_MAX_TOPK || num_shards < 1 ||
       num_shards > DSA_MAX_SHARDS)

@@ -94,6 +94,11 @@ hipError_t launch_cache_write(const PoolView& pool, uint8_t* base, int ikey_fmt,
                               const uint16_t* ikey, const uint16_t* latent, hipStream_t s);
 hipError_t launch_quantize_query(int32_t num_rows, const uint16_t* q, const float* w, uint8_t* qo,
                                  float* wo, hipStream_t s);
+// Both index-key writes and query quantisation in one launch (latents not touched).
+hipError_t launch_indexer_front(const PoolView& pool, uint8_t* base, int ikey_fmt, int32_t n,
+                                const int64_t* slot, const uint16_t* ikey, int32_t num_rows,
+                                const uint16_t* q, const float* w, uint8_t* qo, float* wo,
+                                hipStream_t s);
 
 // Decode context parallelism emulated on one GPU: shard lists and the exact merge.
 size_t dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards);

@@ -156,7 +156,7 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_front_entry_points_validate_before_launch():
-    # dsa_cache_append / dsa_quantize_query: bad arguments are rejected on the host and nothing-to-
+    # dsa_cache_append / dsa_quantize_query / dsa_indexer_front: bad arguments are rejected on the host and nothing-to-
     # do calls return DSA_OK, all without a launch (no GPU here).
     lib = L.lib()
     kv = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_NVFP4, 10, 0.5)
@@ -185,6 +185,19 @@ def test_front_entry_points_validate_before_launch():
     assert lib.dsa_quantize_query(2, ctypes.c_void_p(0x2002), p, p, p, None) == bad
     assert lib.dsa_quantize_query(2, p, p, ctypes.c_void_p(0x2001), p, None) == bad
     assert lib.dsa_quantize_query(0, None, None, None, None, None) == ok
+    # dsa_indexer_front: each half is checked as its own call is, and an empty half needs no
+    # pointers
+    f = lib.dsa_indexer_front
+    assert f(None, pool, 4, p, p, 2, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, -1, p, p, 2, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, p, p, -1, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, None, p, 2, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, p, None, 2, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, p, p, 2, p, None, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, ctypes.c_void_p(0x2004), p, 2, p, p, p, p, None) == bad
+    assert f(ctypes.byref(kv), pool, 4, p, p, 2, p, p, ctypes.c_void_p(0x2001), p, None) == bad
+    assert f(ctypes.byref(kv), pool, 0, None, None, 0, None, None, None, None, None) == ok
+    assert f(ctypes.byref(kvb), pool, 4, p, p, 2, p, p, p, p, None) == L.DSA_ERR_UNSUPPORTED
 
 
 def test_dcp_entry_points_validate_before_launch():

@@ -1,6 +1,7 @@
 """Parity of the step before the path: dsa_cache_append (new tokens quantised into their pool
-rows) and dsa_quantize_query (the FP8 indexer query with its scale folded into the head weight),
-against the oracle's quantisers, bit for bit.
+rows), dsa_quantize_query (the FP8 indexer query with its scale folded into the head weight) and
+dsa_indexer_front (the keys and the query in one launch), against the oracle's quantisers, bit for
+bit.
 
 The pool starts as random bytes; after the calls the whole pool must equal the same random bytes
 with exactly the oracle's codes and scales written at the given slots, so a stray write anywhere
@@ -180,3 +181,55 @@ def test_quantize_query_bit_exact(rows):
     sad.dsa_quantize_query(d_q, d_w, q_idx, d_w)
     torch.cuda.synchronize()
     assert np.array_equal(d_w.cpu().numpy().view(np.uint32), gw.view(np.uint32))
+
+
+@pytest.mark.parametrize("ikey_fmt,n,rows", [
+    (sad.IKEY_FP8, 77, 16),
+    (sad.IKEY_MXFP4, 5, 37),
+    (sad.IKEY_FP8, 0, 3),       # query half only
+    (sad.IKEY_MXFP4, 9, 0),     # key half only
+])
+def test_indexer_front_bit_exact(ikey_fmt, n, rows):
+    """The fused front writes exactly the oracle's index keys (latent bytes untouched) and the
+    oracle's query codes and weights; a latent-only dsa_cache_append afterwards gives the same
+    pool as one dsa_cache_append of both."""
+    print(f"\n[case] indexer_front ikey={ikey_fmt} n={n} rows={rows}", flush=True)
+    rng = np.random.default_rng(3000 + 100 * ikey_fmt + n + rows)
+    nblk = 6
+    kv = sad.kv_layout(ikey_fmt, sad.LATENT_NVFP4, nblk, 0.37)
+    slots = rng.choice(nblk * 64, max(n, 1), replace=False).astype(np.int64)[:n]
+    if n > 3:
+        slots[1] = -1
+        slots[3] = nblk * 64 + 2
+    ikey = _tokens(rng, max(n, 3), 128)[:n]
+    lat = _tokens(rng, max(n, 3), 576)[:n]
+    q = _tokens(rng, max(rows, 1) * 32, 128)[:rows * 32].reshape(rows, 32, 128)
+    w = (rng.standard_normal((rows, 32)) * 0.3).astype(np.float32)
+    host = rng.integers(0, 256, nblk * kv.row_bytes, dtype=np.uint8)
+    pool = torch.from_numpy(host.copy()).cuda()
+    d_slot = torch.from_numpy(slots).cuda() if n else None
+    d_ikey = torch.from_numpy(ikey.view(np.int16)).cuda() if n else None
+    d_q = torch.from_numpy(q.view(np.int16)).cuda() if rows else None
+    d_w = torch.from_numpy(w).cuda() if rows else None
+    q_idx = torch.full((rows, 32, 128), 0x5A, dtype=torch.uint8, device="cuda") if rows else None
+    w_out = torch.full((rows, 32), 7.0, dtype=torch.float32, device="cuda") if rows else None
+    sad.dsa_indexer_front(kv, pool, d_slot, d_ikey, d_q, d_w, q_idx, w_out)
+    torch.cuda.synchronize()
+    want = host.copy()
+    _expected_rows(kv, want, slots, ikey, lat, write_lat=False)
+    got = pool.cpu().numpy()
+    assert np.array_equal(got, want), "keys: " + _first_diff(got, want)
+    if rows:
+        gq, gw = q_idx.cpu().numpy(), w_out.cpu().numpy()
+        for r in range(rows):
+            codes, w2 = oracle.quantize_query(q[r], w[r])
+            assert np.array_equal(gq[r], codes), f"row {r}: " + _first_diff(gq[r].ravel(),
+                                                                             codes.ravel())
+            assert np.array_equal(gw[r].view(np.uint32), w2.view(np.uint32)), f"row {r} weights"
+    if n:
+        d_lat = torch.from_numpy(lat.view(np.int16)).cuda()
+        sad.dsa_cache_append(kv, pool, d_slot, latent=d_lat)
+        pool2 = torch.from_numpy(host.copy()).cuda()
+        sad.dsa_cache_append(kv, pool2, d_slot, index_key=d_ikey, latent=d_lat)
+        torch.cuda.synchronize()
+        assert torch.equal(pool, pool2)
