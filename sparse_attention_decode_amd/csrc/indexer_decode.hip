@@ -14,8 +14,9 @@
 // registers (no LDS staging: each key byte is used by exactly one lane) and scores every row of
 // its row tile from that single read.  The query rows are the MFMA A operand (M = 16 heads, two
 // tiles per row), keys the B operand (N = 16 tokens per tile, K = 128 dims in one instruction),
-// so the head reduction (ReLU, x w, sum over 32 heads) is 8 lane-local terms plus two lane-pair
-// adds (permlane swaps).  The 11-bit radix histogram the exact select needs is built on the way
+// so the head reduction (ReLU, x w, sum over 32 heads) is 8 lane-local terms (an integer max and
+// an FMA each) per token tile, then one three-swap exchange that hands lane group g the sum of
+// token tile g (in the order of a plain xor reduction).  The 11-bit radix histogram the exact select needs is built on the way
 // (LDS atomics, one global atomic per non-empty bin per workgroup).
 #include "dsa_kernels.h"
 
@@ -33,13 +34,13 @@ constexpr int kMaxPagesSmallR = 8;    // one or two rows: the whole run's scores
 struct KeyFrag {
   v8i b;       // MFMA B operand
   int escale;  // MXFP4: E8M0 scale of (token, K block l/16)
-  float scale; // FP8: scale_s of the lane's token
 };
 
 // Byte offsets, within a pool row, of what lane (g, c) reads for token c of a page's first
-// 16-token tile (tile nt adds nt * 16 tokens).
+// 16-token tile (tile nt adds nt * 16 tokens), and of the FP8 scale of token 16g + c, the one
+// token whose score the lane produces.
 struct LaneOffsets {
-  int key, scale;
+  int key, scale, own_scale;
 };
 
 template <int KFMT>
@@ -48,9 +49,11 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const PoolView& p, int g, in
   if (KFMT == DSA_IKEY_FP8) {
     o.key = (int)p.ikey_off + c * DSA_INDEX_DIM + 16 * g;
     o.scale = (int)p.ikey_scale_off + c * 4;
+    o.own_scale = (int)p.ikey_scale_off + (16 * g + c) * 4;
   } else {
     o.key = (int)p.ikey_off + c * (DSA_INDEX_DIM / 2) + 16 * g;
     o.scale = (int)p.ikey_scale_off + c * 4 + g;
+    o.own_scale = 0;
   }
   return o;
 }
@@ -72,9 +75,34 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, int off) {
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
+// max(x, 0) for finite x as one integer max on the bits: a negative float is a negative integer
+// (and -0 becomes +0).  fmaxf would add a NaN-quieting max in front of it.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Head sums of four token tiles at once: lane (g, c) holds partials p[nt] of its four heads for
+// token c of tile nt; it returns the sum over the four lane groups of p[g].  The additions are
+// (g0 + g1) + (g2 + g3), the order of a 16-lane then a 32-lane xor reduction, in three lane swaps
+// instead of eight.
+__device__ __forceinline__ float group_sum_scatter(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows: tiles 0, 1, 0, 1
+  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows: tiles 2, 3, 2, 3
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);            // rows: tiles 0, 1, 2, 3
+}
+
 template <int KFMT, int AUX>
-__device__ __forceinline__ void load_key_page(KeyFrag* f, __amdgpu_buffer_rsrc_t rs,
+__device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu_buffer_rsrc_t rs,
                                               const LaneOffsets& o) {
+  // FP8: scale_s of the one token whose score this lane produces, token 16g + c of the page
+  // (lane group g ends up with the head sum of token tile g); MXFP4 keys carry block scales only
+  if (KFMT == DSA_IKEY_FP8)
+    scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.own_scale, 0, AUX));
+  else
+    scale = 1.0f;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     if (KFMT == DSA_IKEY_FP8) {
@@ -82,13 +110,11 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, __amdgpu_buffer_rsrc_t
       const uint4 lo = ld16<AUX>(rs, k), hi = ld16<AUX>(rs, k + 64);
       f[nt].b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
                     (int)hi.w};
-      f[nt].scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.scale + nt * 64, 0, AUX));
       f[nt].escale = 127;
     } else {
       const uint4 v = ld16<AUX>(rs, o.key + nt * 16 * (DSA_INDEX_DIM / 2));
       f[nt].b = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       f[nt].escale = __builtin_amdgcn_raw_buffer_load_b8(rs, o.scale + nt * 64, 0, AUX);
-      f[nt].scale = 1.0f;
     }
   }
 }
@@ -175,7 +201,8 @@ void indexer_kernel(IndexerArgs a) {
   };
   const LaneOffsets lo = lane_offsets<KFMT>(a.pool, g, c);
   KeyFrag buf[2][4];
-  load_key_page<KFMT, AUX>(buf[0], page_rsrc(0), lo);
+  float bscale[2];
+  load_key_page<KFMT, AUX>(buf[0], bscale[0], page_rsrc(0), lo);
 
   // queries and weights to LDS (the first page is on its way meanwhile)
 #pragma unroll
@@ -200,17 +227,15 @@ void indexer_kernel(IndexerArgs a) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
-      load_key_page<KFMT, AUX>(buf[(u + 1) & 1], page_rsrc(i + 1), lo);  // always issued
+      load_key_page<KFMT, AUX>(buf[(u + 1) & 1], bscale[(u + 1) & 1], page_rsrc(i + 1), lo);  // always issued
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
+      const float cur_scale = bscale[u & 1];
       const int blk = page_of(i);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {  // all R rows (rows past nr score with the last row's query)
-        // Reload the row's query and weights from LDS here: hoisted out of the page loop they
-        // would hold 24 registers per row for the whole kernel.
-        asm volatile("" ::: "memory");
-        v8i qa[2];
-        float wv[2][4];
+      // The rows' queries and weights come from LDS one row ahead of their use, so each row's
+      // reads are in flight while the previous row is scored.  Not hoisted further: out of the
+      // page loop they would hold 24 registers per row for the whole kernel.
+      auto load_row = [&](int r, v8i (&qa)[2], float (&wv)[2][4]) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const uint8_t* qr = &s_q[(r * DSA_INDEX_HEADS + 16 * mt + c) * kQRow];
@@ -221,7 +246,18 @@ void indexer_kernel(IndexerArgs a) {
           const float4 w4 = *reinterpret_cast<const float4*>(&s_w[r * DSA_INDEX_HEADS + 16 * mt + 4 * g]);
           wv[mt][0] = w4.x; wv[mt][1] = w4.y; wv[mt][2] = w4.z; wv[mt][3] = w4.w;
         }
-        float mine = 0.f;
+      };
+      asm volatile("" ::: "memory");
+      v8i qa[2];
+      float wv[2][4];
+      load_row(0, qa, wv);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {  // all R rows (rows past nr score with the last row's query)
+        asm volatile("" ::: "memory");  // at most two rows' queries live
+        v8i qn[2];
+        float wn[2][4];
+        if (r + 1 < R) load_row(r + 1, qn, wn);
+        float pt[4];  // lane-local part of token tile nt's head sum
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -236,18 +272,26 @@ void indexer_kernel(IndexerArgs a) {
           float part = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            part += wv[0][e] * fmaxf(acc0[e], 0.f);
-            part += wv[1][e] * fmaxf(acc1[e], 0.f);
+            part += wv[0][e] * relu(acc0[e]);
+            part += wv[1][e] * relu(acc1[e]);
           }
-          part = xor32_sum(xor16_sum(part));
-          if (g == nt) mine = part * cur[nt].scale;
+          pt[nt] = part;
         }
+        float mine = group_sum_scatter(pt) * cur_scale;
         // materialise the score here: left to the store, the page's whole computation (pure)
         // would be sunk there and every page's key fragments would stay live until then
         asm volatile("" : "+v"(mine));
         sbuf[r][u] = mine;
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
           atomicAdd(&s_hist[((lane % NH) * R + r) * kBins + (order_key(mine) >> 21)], 1u);
+        if (r + 1 < R) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            qa[mt] = qn[mt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[mt][e] = wn[mt][e];
+          }
+        }
       }
     }
   };
