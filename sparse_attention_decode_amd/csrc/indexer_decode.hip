@@ -132,6 +132,14 @@ void indexer_kernel(IndexerArgs a) {
   constexpr int AUX = NT ? 2 : 0;  // cache policy of the key loads
   constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
+  // Three or more rows: two 16-bit bins per LDS word (a workgroup counts at most 64 pages x 4
+  // waves x 64 tokens = 16,384 per row), which halves the histogram's LDS so that three
+  // workgroups fit on a CU.
+  constexpr int HB = R >= 3 ? 2 : 1;  // bins per LDS word
+  constexpr int kHistWords = NH * R * kBins / HB;
+  // The prefill tile reads each row's query a row ahead; fewer rows keep those registers, which
+  // would cost a wave per SIMD.
+  constexpr bool kPrefetchRow = R > 8;
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
   constexpr int kQChunks = R * DSA_INDEX_HEADS * (DSA_INDEX_DIM / 16);  // 16-byte pieces
   constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
@@ -139,7 +147,7 @@ void indexer_kernel(IndexerArgs a) {
   constexpr int kWaves = kThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
-  __shared__ uint32_t s_hist[HIST ? NH * R * kBins : 1];
+  __shared__ uint32_t s_hist[HIST ? kHistWords : 1];
   // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
   const int seq = blockIdx.y / a.tiles_per_seq;
   const int tile = blockIdx.y % a.tiles_per_seq;
@@ -219,7 +227,7 @@ void indexer_kernel(IndexerArgs a) {
     if (i < R * DSA_INDEX_HEADS) s_w[i] = wl[j];
   }
   if (HIST)
-    for (int i = tid; i < NH * R * kBins; i += kThreads) s_hist[i] = 0;
+    for (int i = tid; i < kHistWords; i += kThreads) s_hist[i] = 0;
   lds_barrier();  // not a wait for the first page: the second is requested before that
 
   // Scores of the group of G pages starting at page i0 into sbuf (and the histogram).
@@ -254,9 +262,10 @@ void indexer_kernel(IndexerArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {  // all R rows (rows past nr score with the last row's query)
         asm volatile("" ::: "memory");  // at most two rows' queries live
+        if (!kPrefetchRow && r > 0) load_row(r, qa, wv);
         v8i qn[2];
         float wn[2][4];
-        if (r + 1 < R) load_row(r + 1, qn, wn);
+        if (kPrefetchRow && r + 1 < R) load_row(r + 1, qn, wn);
         float pt[4];  // lane-local part of token tile nt's head sum
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -283,8 +292,12 @@ void indexer_kernel(IndexerArgs a) {
         asm volatile("" : "+v"(mine));
         sbuf[r][u] = mine;
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
-          atomicAdd(&s_hist[((lane % NH) * R + r) * kBins + (order_key(mine) >> 21)], 1u);
-        if (r + 1 < R) {
+        {
+          const uint32_t bin = order_key(mine) >> 21;
+          atomicAdd(&s_hist[(((lane % NH) * R + r) * kBins + bin) / HB],
+                    HB == 2 ? 1u << (16 * (bin & 1)) : 1u);
+        }
+        if (kPrefetchRow && r + 1 < R) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
             qa[mt] = qn[mt];
@@ -317,7 +330,10 @@ void indexer_kernel(IndexerArgs a) {
     for (int i = tid; i < nr * kBins; i += kThreads) {
       uint32_t v = 0;
 #pragma unroll
-      for (int h = 0; h < NH; ++h) v += s_hist[h * R * kBins + i];
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t word = s_hist[(h * R * kBins + i) / HB];
+        v += HB == 2 ? (word >> (16 * (i & 1))) & 0xFFFFu : word;
+      }
       if (v) atomicAdd(&a.hist[(int64_t)(r0 + i / kBins) * kBins + (i % kBins)], v);
     }
   };
