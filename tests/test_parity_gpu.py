@@ -51,6 +51,22 @@ def test_speculative_rows_share_keys():
     check_workload(wl, layer)
 
 
+@pytest.mark.parametrize("rows,ikey", [(2, 0), (3, 1), (5, 0), (7, 1), (8, 0)])
+def test_speculative_rows_per_sequence(rows, ikey):
+    # Each row count is its own scorer instance (rows 3-8 count the histogram in 16-bit halves
+    # of LDS words); the last sequence has fewer rows than the others, one sequence starts its
+    # rows on a block boundary.
+    lens = [3000, 9000 + rows, 64 * 40 + max(1, rows - 2)]
+    rs, rp = [], []
+    for b, L in enumerate(lens):
+        n = rows if b < 2 else max(1, rows - 2)
+        rs += [b] * n
+        rp += [L - n + j for j in range(n)]
+    wl = synth.Workload(f"spec{rows}", 60 + rows, lens, rs, rp, ikey_fmt=ikey, wq=4 if ikey else 8)
+    layer, _, _ = run_gpu(wl)
+    check_workload(wl, layer)
+
+
 @pytest.mark.parametrize("ikey,lat", [(1, 1), (0, 1), (1, 0)])
 def test_decode_low_precision_formats(ikey, lat):
     wl = _one_row_per_seq("lp", 44 + 2 * ikey + lat, [5000, 65, 2049, 12000], ikey_fmt=ikey,
