@@ -36,11 +36,12 @@ struct KeyFrag {
   int escale;  // MXFP4: E8M0 scale of (token, K block l/16)
 };
 
-// Byte offsets, within a pool row, of what lane (g, c) reads for token c of a page's first
-// 16-token tile (tile nt adds nt * 16 tokens), and of the FP8 scale of token 16g + c, the one
-// token whose score the lane produces.
+// Byte offsets, within a pool row, of what lane (g, c) reads: the key bytes of token c of a
+// page's first 16-token tile (tile nt adds nt * 16 tokens), and its scale: FP8, the scale of token
+// 16g + c, the one token whose score the lane produces; MXFP4, the E8M0 scale of token c's K
+// block g (tile nt adds nt * 64 bytes).
 struct LaneOffsets {
-  int key, scale, own_scale;
+  int key, scale;
 };
 
 template <int KFMT>
@@ -48,12 +49,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const PoolView& p, int g, in
   LaneOffsets o;
   if (KFMT == DSA_IKEY_FP8) {
     o.key = (int)p.ikey_off + c * DSA_INDEX_DIM + 16 * g;
-    o.scale = (int)p.ikey_scale_off + c * 4;
-    o.own_scale = (int)p.ikey_scale_off + (16 * g + c) * 4;
+    o.scale = (int)p.ikey_scale_off + (16 * g + c) * 4;
   } else {
     o.key = (int)p.ikey_off + c * (DSA_INDEX_DIM / 2) + 16 * g;
     o.scale = (int)p.ikey_scale_off + c * 4 + g;
-    o.own_scale = 0;
   }
   return o;
 }
@@ -100,7 +99,7 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu
   // FP8: scale_s of the one token whose score this lane produces, token 16g + c of the page
   // (lane group g ends up with the head sum of token tile g); MXFP4 keys carry block scales only
   if (KFMT == DSA_IKEY_FP8)
-    scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.own_scale, 0, AUX));
+    scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.scale, 0, AUX));
   else
     scale = 1.0f;
 #pragma unroll
