@@ -142,8 +142,8 @@ DSA_API dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, i
  *          must be NULL otherwise.
  * Decode and speculative decode (max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ) stream the index keys
  * once per sequence and score all of that sequence's rows from each key read.  Prefill chunks
- * (more rows per sequence; FP8 keys only) score tiles of 16 rows, streaming each key page once per
- * tile.
+ * (more rows per sequence; FP8 or MXFP4 keys) score tiles of 16 rows, streaming each key page once
+ * per tile.
  * Exactness: key products are exact and accumulate in fp32; scale_s > 0 is applied after the
  * head sum (equal to applying it inside each ReLU whenever the sums are exact).
  */

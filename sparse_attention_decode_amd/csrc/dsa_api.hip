@@ -275,9 +275,8 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
                                                  batch->max_context, s),
                       "indexer launch");
   if (hist) return fail(DSA_ERR_INVALID_ARG, "hist must be NULL on the prefill path");
-  if (kv->ikey_format != DSA_IKEY_FP8)
-    return fail(DSA_ERR_UNSUPPORTED, "prefill indexer is built for FP8 keys only");
-  return hip_status(dsa::launch_indexer_prefill(a, batch->max_context, batch->max_rows_per_seq, s),
+  return hip_status(dsa::launch_indexer_prefill(a, kv->ikey_format, batch->max_context,
+                                                batch->max_rows_per_seq, s),
                     "prefill indexer launch");
 }
 

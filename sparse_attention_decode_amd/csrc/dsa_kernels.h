@@ -30,8 +30,8 @@ struct IndexerArgs {
 // Decode / speculative decode scorer: grid (chunks, num_seqs).
 hipError_t launch_indexer_decode(const IndexerArgs& a, int ikey_fmt, int rows_per_seq,
                                  int64_t max_context, hipStream_t s);
-// Prefill scorer (dense FP8 contraction of row tiles x key tiles).
-hipError_t launch_indexer_prefill(const IndexerArgs& a, int64_t max_context,
+// Prefill scorer (dense contraction of row tiles x key tiles; FP8 or MXFP4 keys).
+hipError_t launch_indexer_prefill(const IndexerArgs& a, int ikey_fmt, int64_t max_context,
                                   int32_t max_rows_per_seq, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 

@@ -436,7 +436,7 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
 // contracts one row tile with a run of at most 64 key pages per wave, at least about 2048
 // workgroups in all.  Key pages
 // are re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
-hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
+hipError_t launch_indexer_prefill(const IndexerArgs& a0, int ikey_fmt, int64_t max_context,
                                   int32_t max_rows_per_seq, hipStream_t s) {
   IndexerArgs a = a0;
   constexpr int R = kPrefillRows;
@@ -453,7 +453,8 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a0, int64_t max_context,
   if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
   a.pages_per_wave = (int32_t)ppw;
   dim3 grid((unsigned)((nblk + ppw * kWaves - 1) / (ppw * kWaves)), (unsigned)gy);
-  return launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s);
+  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s)
+                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, R, grid, s);
 }
 
 }  // namespace dsa

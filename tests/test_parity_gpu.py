@@ -101,12 +101,15 @@ def test_physical_rows_and_determinism():
     assert torch.equal(out1, layer.out)
 
 
-def test_prefill_chunk_rows():
-    # 40 rows of one sequence (prefill path: row tiles x key chunks), plus a second sequence.
+@pytest.mark.parametrize("ikey,lat", [(0, 0), (1, 1)])
+def test_prefill_chunk_rows(ikey, lat):
+    # 40 rows of one sequence (prefill path: row tiles x key chunks), plus a second sequence;
+    # FP8 keys and latents, or MXFP4 keys and NVFP4 latents.
     P = 6000
     rs = [0] * 40 + [1] * 12
     rp = [P - 40 + i for i in range(40)] + [900 + i for i in range(12)]
-    wl = synth.Workload("prefill", 47, [P, 912], rs, rp)
+    kw = dict(ikey_fmt=1, lat_fmt=1, wq=4, lat_tensor_scale=0.75) if ikey else {}
+    wl = synth.Workload("prefill", 47 + 3 * ikey, [P, 912], rs, rp, **kw)
     layer, _, _ = run_gpu(wl)
     assert layer.prefill
     check_workload(wl, layer)
