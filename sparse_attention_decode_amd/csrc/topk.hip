@@ -26,6 +26,9 @@ constexpr int kBins = DSA_HIST_BINS;
 constexpr int kFilterThreads = 256;
 constexpr int kPerThread = kTopkSlice / kFilterThreads;  // 16 scores per thread
 constexpr int kHistChunk = 32768;                          // tokens per histogram workgroup
+// Above this many filter slices per row (contexts beyond 256K) the threshold bin is found once
+// per row by its own kernel instead of by every filter workgroup.
+constexpr int kLevel1Slices = 64;
 constexpr int kResolveThreads = 1024;
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kCap = 8192;  // survivors resolved in LDS
@@ -113,17 +116,28 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t* hi
   __syncthreads();
   const float* sc = a.scores + (int64_t)row * a.ld;
   uint32_t* hw = h[wave];
-  for (int s = s0 + threadIdx.x * 4; s < s1; s += 256 * 4) {
-    if (a.vec_ok && s + 3 < s1) {
-      const float4 f = *reinterpret_cast<const float4*>(sc + s);
-      atomicAdd(&hw[order_key(f.x) >> 21], 1u);
-      atomicAdd(&hw[order_key(f.y) >> 21], 1u);
-      atomicAdd(&hw[order_key(f.z) >> 21], 1u);
-      atomicAdd(&hw[order_key(f.w) >> 21], 1u);
-    } else {
+  // four coalesced float4 loads per thread in flight before their counts are added
+  constexpr int kU = 4;
+  for (int base = s0; base < s1; base += 256 * 4 * kU) {
+    float4 f[kU];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (s + j < s1) atomicAdd(&hw[order_key(sc[s + j]) >> 21], 1u);
+    for (int u = 0; u < kU; ++u) {
+      const int s = base + (u * 256 + (int)threadIdx.x) * 4;
+      if (a.vec_ok && s + 3 < s1) f[u] = *reinterpret_cast<const float4*>(sc + s);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = base + (u * 256 + (int)threadIdx.x) * 4;
+      if (a.vec_ok && s + 3 < s1) {
+        atomicAdd(&hw[order_key(f[u].x) >> 21], 1u);
+        atomicAdd(&hw[order_key(f[u].y) >> 21], 1u);
+        atomicAdd(&hw[order_key(f[u].z) >> 21], 1u);
+        atomicAdd(&hw[order_key(f[u].w) >> 21], 1u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (s + j < s1) atomicAdd(&hw[order_key(sc[s + j]) >> 21], 1u);
+      }
     }
   }
   __syncthreads();
@@ -134,6 +148,8 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t* hi
 }
 
 // ------------------------------------------------------------------ filter
+// L1: the threshold bin was found before (topk_level1_kernel); else every workgroup finds it.
+template <bool L1>
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sc[kFilterThreads + 4];
@@ -159,16 +175,20 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a)
     for (int j = 0; j < kPerThread; ++j) v[j] = (j < avail) ? src[j] : 0.f;
   }
 
-  // the histogram row: every load in flight before the first is used
-  const uint32_t* gh = a.hist_in + (int64_t)row * kBins;
-  uint32_t hv[kBins / kFilterThreads];
+  uint32_t b1, rest = 0;
+  if constexpr (L1) {
+    b1 = a.level1[2 * row];
+  } else {
+    // the histogram row: every load in flight before the first is used
+    const uint32_t* gh = a.hist_in + (int64_t)row * kBins;
+    uint32_t hv[kBins / kFilterThreads];
 #pragma unroll
-  for (int j = 0; j < kBins / kFilterThreads; ++j) hv[j] = gh[tid + kFilterThreads * j];
+    for (int j = 0; j < kBins / kFilterThreads; ++j) hv[j] = gh[tid + kFilterThreads * j];
 #pragma unroll
-  for (int j = 0; j < kBins / kFilterThreads; ++j) hist[tid + kFilterThreads * j] = hv[j];
-  __syncthreads();
-  uint32_t rest;
-  const uint32_t b1 = select_bin<kFilterThreads>(hist, kBins, (uint32_t)a.k, &rest, sc, wtot);
+    for (int j = 0; j < kBins / kFilterThreads; ++j) hist[tid + kFilterThreads * j] = hv[j];
+    __syncthreads();
+    b1 = select_bin<kFilterThreads>(hist, kBins, (uint32_t)a.k, &rest, sc, wtot);
+  }
 
   uint32_t mask = 0, cnt = 0;
 #pragma unroll
@@ -184,7 +204,30 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a)
   for (int j = 0; j < kPerThread; ++j)
     if (mask & (1u << j)) out[pos++] = uint2{order_key(v[j]), (uint32_t)(base + kPerThread * tid + j)};
   if (tid == 0) a.slice_cnt[(int64_t)row * a.num_slices + slice] = total;
-  if (tid == 0 && slice == 0) {  // every slice found the same bin; the resolve starts from it
+  if (!L1 && tid == 0 && slice == 0) {  // every slice found the same bin; the resolve starts
+    a.level1[2 * row] = b1;              // from it
+    a.level1[2 * row + 1] = rest;
+  }
+}
+
+// The threshold bin of each row, once, for a filter with many slices per row (prefill): the
+// same search every filter workgroup would otherwise repeat over the row's histogram.
+__global__ __launch_bounds__(kFilterThreads) void topk_level1_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sc[kFilterThreads + 4];
+  __shared__ uint32_t wtot[kFilterThreads / kWave];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  if (a.batch.row_pos[row] + 1 <= a.k) return;
+  const uint32_t* gh = a.hist_in + (int64_t)row * kBins;
+  uint32_t hv[kBins / kFilterThreads];
+#pragma unroll
+  for (int j = 0; j < kBins / kFilterThreads; ++j) hv[j] = gh[tid + kFilterThreads * j];
+#pragma unroll
+  for (int j = 0; j < kBins / kFilterThreads; ++j) hist[tid + kFilterThreads * j] = hv[j];
+  __syncthreads();
+  uint32_t rest;
+  const uint32_t b1 = select_bin<kFilterThreads>(hist, kBins, (uint32_t)a.k, &rest, sc, wtot);
+  if (tid == 0) {
     a.level1[2 * row] = b1;
     a.level1[2 * row + 1] = rest;
   }
@@ -397,8 +440,17 @@ hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStr
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.hist_in = hist_ws;
   }
-  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)a.num_slices, (unsigned)R),
-                     dim3(kFilterThreads), 0, s, a);
+  const bool l1 = a.num_slices > kLevel1Slices;  // many slices per row: find each row's bin once
+  if (l1) {
+    hipLaunchKernelGGL(topk_level1_kernel, dim3((unsigned)R), dim3(kFilterThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (l1)
+    hipLaunchKernelGGL(topk_filter_kernel<true>, dim3((unsigned)a.num_slices, (unsigned)R),
+                       dim3(kFilterThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_filter_kernel<false>, dim3((unsigned)a.num_slices, (unsigned)R),
+                       dim3(kFilterThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)R), dim3(kResolveThreads), 0, s, a);
   return hipGetLastError();
