@@ -138,8 +138,7 @@ DSA_API dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, i
  *          11 bits of each written score's order-preserving key are added to it; dsa_topk
  *          consumes it (saving a pass over the scores) and returns it to zero.  It must be all
  *          zero on entry: allocate it zeroed once, and clear it yourself if scores are computed
- *          without a dsa_topk call.  Only available on the decode path (max_rows_per_seq <= 8);
- *          must be NULL otherwise.
+ *          without a dsa_topk call.  Without it dsa_topk builds the counts in a pass of its own.
  * Decode and speculative decode (max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ) stream the index keys
  * once per sequence and score all of that sequence's rows from each key read.  Prefill chunks
  * (more rows per sequence; FP8 or MXFP4 keys) score tiles of 16 rows, streaming each key page once

@@ -274,7 +274,6 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
     return hip_status(dsa::launch_indexer_decode(a, kv->ikey_format, batch->max_rows_per_seq,
                                                  batch->max_context, s),
                       "indexer launch");
-  if (hist) return fail(DSA_ERR_INVALID_ARG, "hist must be NULL on the prefill path");
   return hip_status(dsa::launch_indexer_prefill(a, kv->ikey_format, batch->max_context,
                                                 batch->max_rows_per_seq, s),
                     "prefill indexer launch");

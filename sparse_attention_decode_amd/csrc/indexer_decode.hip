@@ -25,6 +25,7 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;         // 4 waves
+constexpr int kPrefillThreads = 512;  // the prefill tile with a histogram: 8 waves
 constexpr int kBins = DSA_HIST_BINS;  // top 11 bits of the order-preserving key
 constexpr int kPrefillRows = 16;      // rows per workgroup tile on the prefill path
 constexpr int kMaxPagesPerWave = 64;  // one block-table entry per lane
@@ -125,25 +126,28 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu
 // tile.  Scores stay in registers for G pages and then leave as coalesced 256-byte streaming
 // stores: for one or two rows G covers the whole run, so no store is pending while page loads are
 // (gfx9 counts loads and stores on one counter, and a mix makes every later wait a full drain).
-template <int R, int KFMT, bool HIST, bool NT = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// NTH: threads per workgroup (the prefill tile with a histogram takes 8 waves, so that the one
+// workgroup its LDS allows per CU still puts two waves on each SIMD).
+template <int R, int KFMT, bool HIST, bool NT = false, int NTH = kThreads>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_kernel(IndexerArgs a) {
   constexpr int AUX = NT ? 2 : 0;  // cache policy of the key loads
   constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
-  // Three or more rows: two 16-bit bins per LDS word (a workgroup counts at most 64 pages x 4
-  // waves x 64 tokens = 16,384 per row), which halves the histogram's LDS so that three
-  // workgroups fit on a CU.
+  constexpr int kWaves = NTH / kWave;
+  // Three or more rows: two 16-bit bins per LDS word (a workgroup counts at most 64 pages x
+  // kWaves x 64 tokens, at most 32,768, per row), which halves the histogram's LDS so that three
+  // speculative workgroups, or a 16-row prefill tile with its queries, fit on a CU.
   constexpr int HB = R >= 3 ? 2 : 1;  // bins per LDS word
+  static_assert(HB == 1 || kMaxPagesPerWave * kWaves * kBlock < 65536, "16-bit bins");
   constexpr int kHistWords = NH * R * kBins / HB;
   // The prefill tile reads each row's query a row ahead; fewer rows keep those registers, which
   // would cost a wave per SIMD.
   constexpr bool kPrefetchRow = R > 8;
   constexpr int kQRow = DSA_INDEX_DIM + 16;  // padded LDS row of one head's query
   constexpr int kQChunks = R * DSA_INDEX_HEADS * (DSA_INDEX_DIM / 16);  // 16-byte pieces
-  constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
-  constexpr int kWPer = (R * DSA_INDEX_HEADS + kThreads - 1) / kThreads;
-  constexpr int kWaves = kThreads / kWave;
+  constexpr int kQPer = (kQChunks + NTH - 1) / NTH;
+  constexpr int kWPer = (R * DSA_INDEX_HEADS + NTH - 1) / NTH;
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? kHistWords : 1];
@@ -171,7 +175,7 @@ void indexer_kernel(IndexerArgs a) {
   float wl[kWPer];
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
-    const int i = min(tid + kThreads * j, kQChunks - 1);
+    const int i = min(tid + NTH * j, kQChunks - 1);
     const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
     const int r = rh / DSA_INDEX_HEADS, h = rh % DSA_INDEX_HEADS;
     const int row = r0 + min(r, nr - 1);
@@ -179,7 +183,7 @@ void indexer_kernel(IndexerArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
-    const int i = min(tid + kThreads * j, R * DSA_INDEX_HEADS - 1);
+    const int i = min(tid + NTH * j, R * DSA_INDEX_HEADS - 1);
     const int r = i / DSA_INDEX_HEADS;
     wl[j] = a.w[(int64_t)(r0 + min(r, nr - 1)) * DSA_INDEX_HEADS + i % DSA_INDEX_HEADS];
   }
@@ -214,7 +218,7 @@ void indexer_kernel(IndexerArgs a) {
   // queries and weights to LDS (the first page is on its way meanwhile)
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
-    const int i = tid + kThreads * j;
+    const int i = tid + NTH * j;
     if (i < kQChunks) {
       const int rh = i / (DSA_INDEX_DIM / 16), ch = i % (DSA_INDEX_DIM / 16);
       *reinterpret_cast<uint4*>(&s_q[rh * kQRow + 16 * ch]) = qv[j];
@@ -222,11 +226,11 @@ void indexer_kernel(IndexerArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
-    const int i = tid + kThreads * j;
+    const int i = tid + NTH * j;
     if (i < R * DSA_INDEX_HEADS) s_w[i] = wl[j];
   }
   if (HIST)
-    for (int i = tid; i < kHistWords; i += kThreads) s_hist[i] = 0;
+    for (int i = tid; i < kHistWords; i += NTH) s_hist[i] = 0;
   lds_barrier();  // not a wait for the first page: the second is requested before that
 
   // Scores of the group of G pages starting at page i0 into sbuf (and the histogram).
@@ -326,7 +330,7 @@ void indexer_kernel(IndexerArgs a) {
   };
   auto flush_hist = [&]() {
     lds_barrier();  // every wave's LDS counts are in; its global stores need not be
-    for (int i = tid; i < nr * kBins; i += kThreads) {
+    for (int i = tid; i < nr * kBins; i += NTH) {
       uint32_t v = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
@@ -378,8 +382,12 @@ hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream
     DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
 #undef DSA_CASE
     case kPrefillRows:
-      hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false>), grid, dim3(kThreads), 0,
-                         s, a);
+      if (a.hist)
+        hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, true, false, kPrefillThreads>),
+                           grid, dim3(kPrefillThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false>), grid, dim3(kThreads), 0,
+                           s, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -440,9 +448,9 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a0, int ikey_fmt, int64_t m
                                   int32_t max_rows_per_seq, hipStream_t s) {
   IndexerArgs a = a0;
   constexpr int R = kPrefillRows;
-  constexpr int kWaves = kThreads / kWave;
+  // with a histogram the tile's workgroup has 8 waves (the same waves per CU as two 4-wave ones)
+  const int kWaves = (a.hist ? kPrefillThreads : kThreads) / kWave;
   a.tiles_per_seq = (max_rows_per_seq + R - 1) / R;
-  a.hist = nullptr;
   const int64_t nblk = (max_context + kBlock - 1) / kBlock;
   const int64_t gy = (int64_t)a.batch.num_seqs * a.tiles_per_seq;
   if (gy > 65535) return hipErrorInvalidValue;

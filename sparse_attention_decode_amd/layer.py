@@ -21,8 +21,11 @@ class DSALayer:
         self.prefill = prefill
         R = batch.num_rows
         self.ld = (batch.c.max_context + 63) // 64 * 64
+        # By default the scorer counts the select's histogram on the decode path only: at prefill
+        # the count inside the scorer (8-wave tiles, shared LDS bins) costs about what the
+        # select's own pass saves (prefill-8192: -2%, prefill-2048: +5%).
         decode_path = batch.c.max_rows_per_seq <= L.MAX_ROWS_PER_SEQ
-        self.use_hist = decode_path if use_hist is None else (use_hist and decode_path)
+        self.use_hist = decode_path if use_hist is None else bool(use_hist)
         self.scores = torch.empty((R, self.ld), dtype=torch.float32, device=device)
         # zero on entry to the scorer; dsa_topk returns it to zero after consuming it
         self.hist = (torch.zeros((R, L.HIST_BINS), dtype=torch.int32, device=device)

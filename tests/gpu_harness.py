@@ -13,7 +13,7 @@ import synth.device
 RTOL, ATOL = 2e-2, 2e-3  # bf16 outputs and fp32 log-sum-exp against the float64 oracle
 
 
-def run_gpu(wl: synth.Workload, use_hist=True, prefill=None, zero_qidx=False, phys=True, flags=0):
+def run_gpu(wl: synth.Workload, use_hist=None, prefill=None, zero_qidx=False, phys=True, flags=0):
     kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
     d = synth.device.stage(wl, kv.as_dict())
     if zero_qidx:

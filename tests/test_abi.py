@@ -108,11 +108,11 @@ def test_entry_points_validate_before_launch():
                                  p, None, None, 0, None) == L.DSA_ERR_WORKSPACE
     assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(b3), p, p, p, 2048, 0.1,
                                  p, None, p, need - 1, None) == L.DSA_ERR_WORKSPACE
-    # the prefill path takes no histogram, whatever the key format
+    # the prefill path checks the histogram's alignment like the decode path
     kv4 = sad.kv_layout(sad.IKEY_MXFP4, sad.LATENT_FP8, 10)
     b4 = _fake_batch(max_rows_per_seq=64, num_rows=64)
-    assert lib.dsa_indexer_scores(ctypes.byref(kv4), pool, ctypes.byref(b4), p, p, p, 128, p,
-                                  None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(ctypes.byref(kv4), pool, ctypes.byref(b4), p, p, p, 128,
+                                  ctypes.c_void_p(0x2002), None) == L.DSA_ERR_INVALID_ARG
     assert lib.dsa_status_string(L.DSA_ERR_WORKSPACE) == b"DSA_ERR_WORKSPACE"
 
 

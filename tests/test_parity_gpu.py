@@ -101,17 +101,20 @@ def test_physical_rows_and_determinism():
     assert torch.equal(out1, layer.out)
 
 
-@pytest.mark.parametrize("ikey,lat", [(0, 0), (1, 1)])
-def test_prefill_chunk_rows(ikey, lat):
+@pytest.mark.parametrize("ikey,lat,hist", [(0, 0, False), (1, 1, False), (0, 0, True), (1, 0, True)])
+def test_prefill_chunk_rows(ikey, lat, hist):
     # 40 rows of one sequence (prefill path: row tiles x key chunks), plus a second sequence;
     # FP8 keys and latents, or MXFP4 keys and NVFP4 latents.
     P = 6000
     rs = [0] * 40 + [1] * 12
     rp = [P - 40 + i for i in range(40)] + [900 + i for i in range(12)]
-    kw = dict(ikey_fmt=1, lat_fmt=1, wq=4, lat_tensor_scale=0.75) if ikey else {}
-    wl = synth.Workload("prefill", 47 + 3 * ikey, [P, 912], rs, rp, **kw)
-    layer, _, _ = run_gpu(wl)
-    assert layer.prefill
+    # hist: the scorer counts the select's histogram itself (8-wave prefill tiles)
+    kw = dict(ikey_fmt=1, wq=4) if ikey else {}
+    if lat:
+        kw.update(lat_fmt=1, lat_tensor_scale=0.75)
+    wl = synth.Workload("prefill", 47 + 3 * ikey + lat, [P, 912], rs, rp, **kw)
+    layer, _, _ = run_gpu(wl, use_hist=hist)
+    assert layer.prefill and (layer.hist is not None) == hist
     check_workload(wl, layer)
 
 
