@@ -335,8 +335,12 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
 #pragma unroll
   for (int j = 0; j < kBins / kResolveThreads; ++j) hist_row[tid + kResolveThreads * j] = 0;
 
-  // levels 2 and 3: key bits [20:10] and [9:0] among survivors sharing the chosen prefix
+  // levels 2 and 3: key bits [20:10] and [9:0] among survivors sharing the chosen prefix.  When
+  // the cut takes the whole level-2 bin (the usual case: a few hundred survivors share the top
+  // 11 bits, spread over 2,048 level-2 bins), every key at or above that 21-bit prefix is in and
+  // level 3 is skipped.
   uint32_t prefix = b1 << 21, mask = 0xFFE00000u;
+  bool whole_bin = false;
 #pragma unroll
   for (int lev = 0; lev < 2; ++lev) {
     const int shift = lev == 0 ? 10 : 0;
@@ -354,9 +358,16 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     need = rest;
     prefix |= b << shift;
     mask |= bmask << shift;
+    if (lev == 0 && prefix != 0u && need == sh.hist[b]) {  // uniform
+      whole_bin = true;
+      break;
+    }
   }
-  const uint32_t T = prefix;  // exact key of the k-th largest score
-  const uint32_t E = need;    // keys equal to T that make the cut (the lowest-index ones)
+  // The cut: keys above T, and of the keys equal to T the E with the lowest token index.  T is
+  // the exact key of the k-th largest score, or, when the whole level-2 bin is taken, the key
+  // just below that bin (and E = 0).
+  const uint32_t T = whole_bin ? prefix - 1u : prefix;
+  const uint32_t E = whole_bin ? 0u : need;
   if (bt_cached) {
 #pragma unroll
     for (int j = 0; j < kBtPer; ++j) {
