@@ -147,3 +147,29 @@ def test_prefill_first_chunk_from_position_zero():
     layer, _, _ = run_gpu(wl)
     assert layer.prefill
     check_workload(wl, layer)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_batches(case):
+    """Seeded random batches: 1-5 sequences of 1-20,000 tokens, 1-8 rows per sequence (or a
+    prefill chunk of 9-40 rows), k from {1, 63, 512, 2048}, every key and latent format, with or
+    without the scorer's histogram, all against the oracle."""
+    rng = np.random.default_rng(9000 + case)
+    nseq = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(1, 20001, nseq)]
+    prefill = case % 4 == 3
+    rs, rp = [], []
+    for b, L in enumerate(lens):
+        n = int(rng.integers(9, 41)) if (prefill and b == 0) else int(rng.integers(1, 9))
+        n = min(n, L)
+        rs += [b] * n
+        rp += [L - n + j for j in range(n)]
+    ikey, lat = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    kw = dict(ikey_fmt=ikey, lat_fmt=lat, wq=4 if ikey else 8,
+              lat_tensor_scale=0.75 if lat else 1.0, k=int(rng.choice([1, 63, 512, 2048])))
+    wl = synth.Workload(f"rand{case}", 9000 + case, lens, rs, rp, **kw)
+    hist = bool(rng.integers(0, 2))
+    print(f"\n[case] random {case}: lens={lens} rows={len(rs)} ikey={ikey} lat={lat} "
+          f"k={kw['k']} hist={hist}", flush=True)
+    layer, _, _ = run_gpu(wl, use_hist=hist)
+    check_workload(wl, layer)
