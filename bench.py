@@ -273,7 +273,7 @@ def main():
                     help="replay select + attention from a HIP graph per batch (slower on this "
                          "stack than five eager launches: the replay adds GPU-side time)")
     ap.add_argument("--no-graph", action="store_true", help="the default; kept for old commands")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=8,
                     help="time the scorer with a pair of events on every n-th timed step (each "
                          "pair costs the step a few microseconds)")
     ap.add_argument("--no-cpu", action="store_true")
