@@ -641,13 +641,29 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
 int mla_num_splits(int32_t num_rows, int32_t k, bool invariant) {
   if (invariant) return (k + 4 * kTile - 1) / (4 * kTile);
   const int tiles = (k + kTile - 1) / kTile;
-  int want = (DSA_MLA_TARGET_WGS + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
-  if (want > tiles) want = tiles;
+  const int64_t rows = num_rows > 0 ? num_rows : 1;
   // at most 32 splits (64 tokens each at k = 2,048): below that size a split is one tile, and the
   // combine's extra round over the slots costs more than the parallelism gains (one row: 1.4 us)
-  if (want > DSA_MLA_MAX_SPLITS) want = DSA_MLA_MAX_SPLITS;
-  if (want < 1) want = 1;
-  return want;
+  const int cap = tiles < DSA_MLA_MAX_SPLITS ? tiles : DSA_MLA_MAX_SPLITS;
+  // One workgroup fits a CU (its LDS), so a launch of rows x ns workgroups runs in
+  // ceil(rows ns / 256) waves of workgroups, each lasting about kFixedTiles + (tiles per split)
+  // tile-times (the fixed part: query and pool-row loads, the first gathers' round trip, the
+  // partial stores).  The split count with the least of that wins, the fewest splits on a tie
+  // (less for the combine): 96 speculative rows take 5 splits (two waves of 13 tiles) rather than
+  // 3 (two waves of 22), 16 decode rows 16, one row 32.
+  constexpr int64_t kFixedTiles = 3;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int ns = 1; ns <= cap; ++ns) {
+    const int64_t per = (tiles + ns - 1) / ns;
+    const int64_t waves = (rows * ns + DSA_MLA_TARGET_WGS - 1) / DSA_MLA_TARGET_WGS;
+    const int64_t cost = waves * (kFixedTiles + per);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ns;
+    }
+  }
+  return best;
 }
 
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant) {
