@@ -27,8 +27,12 @@
  * tables; scores against hand-worked fixtures, one-hot closed forms, q = 0, scale pull-out and
  * head-permutation invariance; top-k against its defining order property and brute force on
  * tiny inputs; attention against float64 scaled-dot-product attention from torch when the
- * selected set is every visible token, against single-token / identical-latent / q = 0 closed
- * forms, and against permutation and causality invariants; quantisers against an arithmetic
+ * selected set is every visible token, and, when it is a strict subset (k below the visible
+ * count), against the same attention over latents decoded independently (torch's E4M3 cast, the
+ * OCP E2M1 table) at the selected indices with their own scales; FP8 latent dequantisation
+ * against a hand-worked fixture with a distinct scale per token; attention against single-token
+ * / identical-latent / q = 0 closed forms, and against permutation and causality invariants;
+ * quantisers against an arithmetic
  * round-half-even formulation on each format's grid, midpoints, saturation, exact round trips of
  * representable tokens, the scale rules and error bounds of each format, and the query-scale fold
  * through the scoring rule.

@@ -264,6 +264,17 @@ def test_mla_selected_order_invariance():
     assert np.allclose(a, b, rtol=1e-12, atol=1e-14) and np.allclose(la, lb, rtol=1e-13)
 
 
+def test_fp8_latent_dequant_hand_worked():
+    # distinct per-token scales: a dropped or inverted scale, or one taken from the wrong token,
+    # changes the values written out by hand in the fixture
+    g = _load("latent_fp8_tiny.json")
+    v = oracle.dequant_latent_fp8(np.array(g["codes"], np.uint8),
+                                  np.array(g["scales"], np.float32))
+    want = np.array(g["values"], np.float64)
+    assert np.array_equal(v, want)
+    assert np.array_equal(np.signbit(v), np.signbit(want))
+
+
 def test_nvfp4_latent_dequant_hand_worked():
     # byte 0x53: element 0 = nibble 3 (1.5), element 1 = nibble 5 (3.0); block scale 0x38 = 1.0;
     # byte 0xF8: element 2 = nibble 8 (-0), element 3 = nibble 0xF (-6); tensor scale 0.5.
@@ -324,3 +335,49 @@ def test_layer_selected_set_is_the_defining_top_k():
     for i, p in enumerate(wl.row_pos):
         s = res["scores"][i, :p + 1]
         _check_topk_property(s, 2048, res["idx"][i], res["count"][i])
+
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _latents_from_codes(wl, lat, ls, sel):
+    """Dequantised latents of the tokens `sel`, built here from the stored codes with torch's
+    E4M3 cast and the OCP E2M1 table (not through the oracle's decoders): FP8, code times the
+    token's own scale; NVFP4, E2M1 element times its block's E4M3 scale times the tensor scale."""
+    f8 = lambda c: torch.from_numpy(np.ascontiguousarray(c, np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+    if wl.lat_fmt == 0:
+        return f8(lat[sel]) * ls[sel].astype(np.float64)[:, None]
+    packed = lat[sel]
+    nib = np.empty((len(sel), 576), np.uint8)
+    nib[:, 0::2] = packed & 0xF
+    nib[:, 1::2] = packed >> 4
+    val = np.where(nib & 8, -1.0, 1.0) * _E2M1[nib & 7]
+    bs = np.repeat(f8(ls[sel]), 16, axis=1)
+    return val * bs * float(wl.lat_tensor_scale)
+
+
+@pytest.mark.parametrize("ikey,lat", [(0, 0), (1, 1)])
+def test_layer_attention_over_a_strict_subset(ikey, lat):
+    # k < visible tokens at interior positions: the attention runs over exactly the selected
+    # tokens, each latent taken at its own token index with its own scale.  The reference is
+    # float64 SDPA over latents gathered at the oracle's own idx and decoded independently.
+    wl = _tiny_workload(24, 3000, [1500, 2999, 2203], 256, ikey, lat)
+    res = oracle.workload_rows(wl, 0)
+    _, _, latc, ls = synth.seq_tensors(wl, 0)
+    _, _, qm = synth.row_queries(wl)
+    for i, p in enumerate(wl.row_pos):
+        cnt = int(res["count"][i])
+        sel = res["idx"][i, :cnt]
+        assert cnt == 256 and np.all(res["idx"][i, cnt:] == -1)
+        # a strict, non-trivial subset: slot j does not hold token j
+        assert sel.max() <= p and np.count_nonzero(sel != np.arange(cnt)) > cnt // 2
+        c = _latents_from_codes(wl, latc, ls, sel)
+        qf = torch.from_numpy(oracle.bf16(qm[i]))  # [96, 576]
+        ct = torch.from_numpy(c)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qf[None, :, None, :], ct[None, None].expand(1, 96, cnt, 576),
+            ct[None, None, :, :512].expand(1, 96, cnt, 512), scale=wl.softmax_scale)[0, :, 0]
+        ref_lse = torch.logsumexp(qf @ ct.T * wl.softmax_scale, dim=-1)
+        assert np.allclose(res["out"][i], ref.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(res["lse"][i], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
