@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of one DSA layer step (indexer scores -> exact top-2048 -> sparse MLA) on one MI355X.
 
-Default workload: batched decode, 16 sequences x 1 query row, each with 131,072 cached tokens,
-FP8 index keys (132 B/token) and FP8 latents (576 B + 4 B scale per token) in 64-token paged
-blocks from one shuffled pool, 96 MLA heads, top-k 2048.  A step processes one batch of 16 rows;
-consecutive steps rotate over independent batches (separate pools) so the 277 MB key stream is
-read from HBM rather than from the 256 MB memory-side cache.  Inputs are resident in HBM before
-the timed region.  Prints one JSON line.
+Default workload (the largest decode shape): speculative decode, 16 sequences x 6 query rows
+(1 + 5 draft tokens, causal within the step) at a context of 1,048,576 tokens each, FP8 index keys
+(132 B/token) and FP8 latents (576 B + 4 B scale per token) in 64-token paged blocks from one
+shuffled 11.95 GB pool, 96 MLA heads, top-k 2048 per row.  The 2.2 GB of keys a step reads are far
+larger than the 256 MB memory-side cache, so every step streams them from HBM.  Other workloads (--config): 0 decode-1x8K, 1 decode-16x128K (four rotated
+batches), 3 prefill-8192-on-339968, 4 mixed-64-mxfp4-nvfp4, 5 prefill-2048-on-150000.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..5] [--graph]
 """
@@ -98,35 +99,49 @@ def recorded_traffic(workload: str):
 
 
 def cpu_baseline(cfg: int, wl, budget_s: float = 15.0):
-    """The oracle, as it stands, on a bounded sample of the workload: each of (up to) 16 rows
-    spread over the batch is generated once and evaluated repeatedly by the oracle (whole layer:
-    fp64 + fp32 scores, sort, fp64 attention) until its share of the budget is used.  Returns
-    query rows per second on the host's cores."""
+    """The oracle, as it stands, on a bounded sample of the workload: whole sequences spread over
+    the batch with at most 16 rows in all (decode-16x128K: its 16 single-row sequences;
+    specdec-16x6-1M: one sequence with its 6 rows), each sequence's inputs generated once and its
+    rows evaluated together by the oracle (whole layer: fp64 + fp32 scores, sort, fp64
+    attention), repeated until the sequence's share of the budget is used.  Returns query rows per
+    second on the host's cores."""
     import numpy as np
     import oracle
     import synth
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    picks = list(range(wl.num_rows))[::max(1, wl.num_rows // 16)][:16]
-    share = budget_s / len(picks)
-    calls, spent = 0, 0.0
-    for r in picks:
-        b = int(wl.row_seq[r])
-        n = int(wl.row_pos[r]) + 1
-        keys, ks, lat, ls = synth.seq_tensors(wl, b, n)
-        qi, hw = synth.qidx(wl.seed, int(wl.row_id[r]), 1, wl.wq)
-        qm = synth.qmla(wl.seed, int(wl.row_id[r]), 1)
-        row_spent = 0.0
-        while row_spent < share or row_spent == 0.0:
+    per_seq = max(len(wl.rows_of(b)) for b in range(wl.num_seqs))
+    nseq = min(wl.num_seqs, 16) if per_seq == 1 else 1
+    seqs = list(range(wl.num_seqs))[::max(1, wl.num_seqs // nseq)][:nseq]
+    share = budget_s / len(seqs)
+    rows_done, spent, picked = 0, 0.0, []
+    for b in seqs:
+        rows = wl.rows_of(b)
+        if len(rows) > 16:  # a prefill chunk: 16 rows spread over it
+            rows = rows[::max(1, len(rows) // 16)][:16]
+        picked += [int(r) for r in rows]
+        need = int(wl.row_pos[rows].max()) + 1
+        keys, ks, lat, ls = synth.seq_tensors(wl, b, need)
+        qi = np.empty((len(rows), 32, 128), np.uint8)
+        hw = np.empty((len(rows), 32), np.float32)
+        qm = np.empty((len(rows), 96, 576), np.uint16)
+        for i, r in enumerate(rows):
+            a, c = synth.qidx(wl.seed, int(wl.row_id[r]), 1, wl.wq)
+            qi[i], hw[i] = a[0], c[0]
+            qm[i] = synth.qmla(wl.seed, int(wl.row_id[r]), 1)[0]
+        seq_spent = 0.0
+        while seq_spent < share or seq_spent == 0.0:
             t0 = time.perf_counter()
-            oracle.dsa_rows(wl.ikey_fmt, wl.lat_fmt, wl.row_pos[[r]], qi, hw, qm, keys, ks, lat,
+            oracle.dsa_rows(wl.ikey_fmt, wl.lat_fmt, wl.row_pos[rows], qi, hw, qm, keys, ks, lat,
                             ls, wl.lat_tensor_scale, wl.k, wl.softmax_scale)
-            row_spent += time.perf_counter() - t0
-            calls += 1
-        spent += row_spent
-    return {"value": calls / spent, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} oracle evaluations of {len(picks)} of the {wl.num_rows} rows of "
-                      f"{wl.name} (rows {picks}), whole layer per row (scores in fp64 and fp32, "
-                      f"top-k by sort, fp64 attention), {spent:.1f} s on {threads} threads"}
+            seq_spent += time.perf_counter() - t0
+            rows_done += len(rows)
+        spent += seq_spent
+    return {"value": rows_done / spent, "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows_done} row evaluations of {len(picked)} of the {wl.num_rows} rows of "
+                      f"{wl.name} (rows {picked[:16]}), whole layer per row (scores in fp64 and "
+                      f"fp32, top-k by sort, fp64 attention; inputs generated once, outside the timing), "
+                      f"{spent:.1f} s on {threads} threads"}
 
 
 def time_front(wl, d, kv, steps: int):
@@ -170,6 +185,51 @@ def time_front(wl, d, kv, steps: int):
     return {"entry_points": "dsa_indexer_front + dsa_cache_append(latents)", "new_tokens": R,
             "query_rows": R, "us_per_step": us, "algorithmic_bytes_per_step": nbytes,
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9}
+
+
+def read_ceiling(wls, devs, kvs, reps: int = 10):
+    """Measured read ceilings after the timed region (dsa_probe_read: loads only, no
+    arithmetic): (a) exactly the scorer's key pages, block by block in the block tables' order,
+    rotating over the same batches as the timed steps; (b) a contiguous read of as many bytes from
+    the start of each pool.  Returns GB/s of each (event-timed, `reps` launches)."""
+    import torch
+    import sparse_attention_decode_amd as sad
+    key_page = 64 * (132 if wls[0].ikey_fmt == 0 else 68)
+    rows_list, npages = [], 0
+    for wl, d in zip(wls, devs):
+        bt = []
+        for b in range(wl.num_seqs):
+            L = int(wl.row_pos[wl.rows_of(b)].max()) + 1
+            bt.append(np.asarray(wl.block_table[b, :(L + 63) // 64], np.int32))
+        r = np.concatenate(bt)
+        rows_list.append(torch.from_numpy(r).cuda())
+        npages = r.size
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name in ("pages", "sequential"):
+        def run(j):
+            kv, d = kvs[j], devs[j]
+            if name == "pages":
+                sad.dsa_probe_read(d["pool"], kv.row_bytes, kv.ikey_off, key_page, rows_list[j],
+                                   rows_list[j].numel(), sink)
+            else:
+                sad.dsa_probe_read(d["pool"], key_page, 0, key_page, None,
+                                   rows_list[j].numel(), sink)
+        for i in range(3):
+            run(i % len(devs))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            run(i % len(devs))
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / reps
+        res[name + "_GBps"] = npages * key_page / (us * 1e-6) / 1e9
+    res["bytes_per_launch"] = npages * key_page
+    res["launches"] = reps
+    return res
 
 
 def bench_dcp(args):
@@ -267,15 +327,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--replicas", type=int, default=0, help="independent batches (0: auto)")
     ap.add_argument("--graph", action="store_true",
                     help="replay select + attention from a HIP graph per batch (slower on this "
                          "stack than five eager launches: the replay adds GPU-side time)")
     ap.add_argument("--no-graph", action="store_true", help="the default; kept for old commands")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=1,
                     help="time the scorer with a pair of events on every n-th timed step (each "
-                         "pair costs the step a few microseconds)")
+                         "pair costs the step a few microseconds: under 1%% of a speculative "
+                         "step, about 5%% of a decode-16x128K step)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the read-ceiling probe after the timed region")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--dcp", type=int, default=0,
@@ -381,7 +444,8 @@ def main():
         step(i, evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    idx_ms = sum(a.elapsed_time(b) for a, b in evs.values()) / len(evs)
+    idx_samples = sorted(a.elapsed_time(b) for a, b in evs.values())
+    idx_ms = sum(idx_samples) / len(idx_samples)
 
     wl = wls[0]
     rows = wl.num_rows
@@ -401,8 +465,15 @@ def main():
     roof["traffic"] = None if prefill else recorded_traffic(wl.name)
     roof["kernel"] = "indexer_kernel (dsa_indexer_scores)"
     roof["ms_per_launch"] = idx_ms
+    roof["ms_per_launch_median"] = idx_samples[len(idx_samples) // 2]
     roof["timed_launches"] = len(evs)
+    roof["timing"] = "hip events on the scorer's stream around its launch in the timed steps"
     roof["algorithmic_bytes_per_launch"] = idx_b
+    roof["layer_frac"] = layer_gbps / PEAK_HBM_GBPS
+    if not prefill and not args.no_probe:
+        ceil = read_ceiling(wls, devs, kvs)
+        roof["measured_ceiling"] = ceil
+        roof["frac_of_page_ceiling"] = roof["achieved"] / ceil["pages_GBps"]
 
     result = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,

@@ -20,12 +20,17 @@
  * Conventions for every entry point:
  *   - Pointers are device pointers unless the comment says "host".  The caller owns every
  *     buffer (pool, tables, queries, outputs, workspaces); the library never allocates or frees
- *     device memory and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is
- *     the default stream) and buffers must stay valid until it completes.
+ *     device memory and never synchronises (dsa_device_status alone waits for its stream): work
+ *     is enqueued on `stream` (a hipStream_t of the current device; NULL is the default stream)
+ *     and buffers must stay valid until it completes.
  *   - Errors are returned, never thrown.  Host-side validation runs before anything is launched;
  *     a failed call launches nothing.  dsa_last_error() gives a per-thread message.
- *   - Out-of-range device data (a block id outside the pool, an index past a row's position) is
- *     not checked on the device; results are then undefined.
+ *   - Device data that breaks the contract is detected where it is read and recorded in a
+ *     per-device status word (DSA_DEVERR_* bits below; dsa_device_status reads and clears it):
+ *     a block-table entry outside the pool (the scorer scores that block's tokens as 0, the
+ *     attention skips them), a pool row past the pool given to the attention (skipped), a
+ *     sequence with more rows than max_rows_per_seq (its extra rows are not scored).  Selected
+ *     indices outside [0, row position] are ignored by the attention (-1 is the padding).
  *   - Identical inputs give bit-identical outputs.
  */
 #ifndef DSA_H_
@@ -122,6 +127,13 @@ typedef struct dsa_batch {
  * Without it the split count follows the row count (faster; outputs then agree within rounding
  * between batches of different row counts).  Scores and the select are batch-invariant always. */
 #define DSA_BATCH_INVARIANT 1u
+
+/* Bits of the device status word.  Once set, a bit stays set until dsa_device_status clears it;
+ * while DSA_DEVERR_ROWS_PER_SEQ is set, every dsa_topk on that device writes count = -1 and
+ * idx = phys = -1 for all of its rows (the rows a scorer skipped have no scores to select from). */
+#define DSA_DEVERR_ROWS_PER_SEQ 1u /* a sequence had more rows than dsa_batch.max_rows_per_seq */
+#define DSA_DEVERR_BLOCK_ID 2u     /* a block-table entry of a visible block was outside the pool */
+#define DSA_DEVERR_POOL_ROW 4u     /* a physical row given to the attention was past the pool */
 
 /* Fill *out (host) with the pool layout for the given formats (block_size must be 64).
  * Returns INVALID_ARG for a null pointer or bad value, UNSUPPORTED for another block size. */
@@ -339,6 +351,23 @@ DSA_API dsa_status sparse_mla_decode_shard(const dsa_kv_layout* kv, const void* 
 DSA_API dsa_status dsa_lse_combine(int32_t num_rows, int32_t k, int32_t num_shards, uint32_t flags,
                                    const void* partials, size_t partials_bytes, uint16_t* out,
                                    float* lse, void* stream);
+
+/* Measurement only (computes nothing of the method): stream num_pages pages of bytes_per_page
+ * bytes each, page i at base + (rows ? rows[i] : i) * row_bytes + offset, with no arithmetic
+ * behind the loads, on `grid` workgroups that each leave one word (the XOR of what they read) in
+ * sink[grid].  With rows = the physical blocks a scorer visits and offset = the key page, this is
+ * the ceiling of the scorer's access pattern; with rows = NULL and row_bytes = bytes_per_page, a
+ * contiguous read.  bytes_per_page: a multiple of 16 up to 9,216; base + offset and row_bytes
+ * 16-byte aligned; grid in [1, 65535].  Every page must lie in memory the caller owns. */
+DSA_API dsa_status dsa_probe_read(const void* base, int64_t row_bytes, int64_t offset,
+                                  int32_t bytes_per_page, const int32_t* rows, int64_t num_pages,
+                                  uint32_t* sink, int32_t grid, void* stream);
+
+/* The status word of the current device (DSA_DEVERR_* bits, 0 when every call so far met its
+ * contract).  This call synchronises `stream` (which must belong to the current device) before
+ * reading, so the word covers all work enqueued on it; clear != 0 then resets the word to 0.
+ * Work on other streams that is still running may set bits after the read. */
+DSA_API dsa_status dsa_device_status(uint32_t* status, int32_t clear, void* stream);
 
 /* Text of a status code, and the calling thread's last error message ("" if none). */
 DSA_API const char* dsa_status_string(dsa_status s);

@@ -21,8 +21,11 @@ EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes
            "sparse_mla_decode", "sparse_mla_prefill", "dsa_cache_append", "dsa_quantize_query",
            "dsa_indexer_front",
            "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_dcp_partials_bytes",
-           "sparse_mla_decode_shard", "dsa_lse_combine", "dsa_status_string", "dsa_last_error")
+           "sparse_mla_decode_shard", "dsa_lse_combine", "dsa_device_status", "dsa_probe_read", "dsa_status_string",
+           "dsa_last_error")
 MERGE_PACKED, MERGE_SCORES, MERGE_GENERIC, MAX_SHARDS = 0, 1, 2, 8
+# bits of the device status word (include/dsa.h)
+DEVERR_ROWS_PER_SEQ, DEVERR_BLOCK_ID, DEVERR_POOL_ROW = 1, 2, 4
 
 
 class DSAError(RuntimeError):
@@ -103,6 +106,10 @@ def lib():
                                               vp, vp, vp, vp, i32, f32, i32, i32, vp, sz, vp]
         L.dsa_lse_combine.restype = i32
         L.dsa_lse_combine.argtypes = [i32, i32, i32, ctypes.c_uint32, vp, sz, vp, vp, vp]
+        L.dsa_probe_read.restype = i32
+        L.dsa_probe_read.argtypes = [vp, i64, i64, i32, vp, i64, vp, i32, vp]
+        L.dsa_device_status.restype = i32
+        L.dsa_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32, vp]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [i32]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -273,3 +280,21 @@ def dsa_lse_combine(num_rows: int, k: int, num_shards: int, partials, out, lse=N
     _check(lib().dsa_lse_combine(num_rows, k, num_shards, flags, _ptr(partials),
                                  _nbytes(partials), _ptr(out), _ptr(lse), _stream(stream)),
            "dsa_lse_combine")
+
+
+def dsa_device_status(clear: bool = True, stream=None) -> int:
+    """The device status word (DEVERR_* bits) after the work enqueued on `stream`; synchronises
+    that stream, and resets the word to 0 when `clear`."""
+    v = ctypes.c_uint32(0)
+    _check(lib().dsa_device_status(ctypes.byref(v), 1 if clear else 0, _stream(stream)),
+           "dsa_device_status")
+    return int(v.value)
+
+
+def dsa_probe_read(base, row_bytes: int, offset: int, bytes_per_page: int, rows, num_pages: int,
+                   sink, stream=None):
+    """Measurement only: stream num_pages pages (see include/dsa.h); sink: uint32/int32 device
+    tensor with one word per workgroup (its length is the grid)."""
+    _check(lib().dsa_probe_read(_ptr(base), row_bytes, offset, bytes_per_page, _ptr(rows),
+                                num_pages, _ptr(sink), sink.numel(), _stream(stream)),
+           "dsa_probe_read")

@@ -3,11 +3,18 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "dsa_kernels.h"
+
+// The device status word (DSA_DEVERR_* bits): one per device, set by the kernels with atomic ORs
+// where they meet device data outside the contract, read and cleared by dsa_device_status.  Host
+// code never uses this name as an address: each device's address comes from hipGetSymbolAddress.
+static __device__ uint32_t dev_status;
 
 namespace {
 
@@ -27,6 +34,50 @@ dsa_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t*> g_status[kMaxDevices];
+std::mutex g_symbol_mu;
+
+// The current device, checked against the device of `stream` (kernels get addresses of this
+// device's status word, so they must run on it).
+dsa_status current_device(hipStream_t stream, int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (*dev < 0 || *dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d beyond the %d this build tracks", *dev, kMaxDevices);
+  if (stream) {
+    hipDevice_t sd;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sd != *dev)
+      return fail(DSA_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d",
+                  (int)sd, *dev);
+  }
+  return DSA_OK;
+}
+
+// Address of the current device's status word, looked up once per device.
+dsa_status status_word(hipStream_t stream, uint32_t** out) {
+  int dev;
+  dsa_status st = current_device(stream, &dev);
+  if (st != DSA_OK) return st;
+  uint32_t* p = g_status[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_symbol_mu);
+    p = g_status[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(dev_status));
+      if (e != hipSuccess || !addr)
+        return fail(DSA_ERR_HIP, "hipGetSymbolAddress(status word): %s", hipGetErrorString(e));
+      p = static_cast<uint32_t*>(addr);
+      g_status[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DSA_OK;
+}
 
 dsa_status check_layout(const dsa_kv_layout* kv, const void* pool) {
   if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is NULL");
@@ -147,8 +198,9 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
     if (!aligned(q, 16)) return fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
   } else {
     if (!q || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, idx and out must be non-NULL");
-    if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    if (!aligned(q, 16) || !aligned(out, 16))
       return fail(DSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   }
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
   if (!isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale not finite");
@@ -192,6 +244,7 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
     if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
     partial_views(a, workspace, batch->num_rows);
   }
+  if ((st = status_word(stream, &a.status)) != DSA_OK) return st;
   return hip_status(dsa::launch_sparse_mla(a, kv->latent_format, shard < 0, stream),
                     shard >= 0 ? "sparse_mla_decode_shard launch"
                                : (prefill ? "sparse_mla_prefill launch" : "sparse_mla_decode launch"));
@@ -213,6 +266,53 @@ const char* dsa_status_string(dsa_status s) {
 }
 
 const char* dsa_last_error(void) { return g_err; }
+
+dsa_status dsa_probe_read(const void* base, int64_t row_bytes, int64_t offset,
+                          int32_t bytes_per_page, const int32_t* rows, int64_t num_pages,
+                          uint32_t* sink, int32_t grid, void* stream) {
+  g_err[0] = 0;
+  if (!base || !sink) return fail(DSA_ERR_INVALID_ARG, "base and sink must be non-NULL");
+  if (bytes_per_page < 16 || bytes_per_page % 16 || bytes_per_page > 16 * dsa::kProbeMaxPieces)
+    return fail(DSA_ERR_INVALID_ARG, "bytes_per_page %d not a multiple of 16 in [16, %d]",
+                bytes_per_page, 16 * dsa::kProbeMaxPieces);
+  if (offset < 0 || row_bytes < 0 || row_bytes % 16 || !aligned((const uint8_t*)base + offset, 16))
+    return fail(DSA_ERR_INVALID_ARG, "base + offset and row_bytes must be 16-byte aligned");
+  if (num_pages < 0) return fail(DSA_ERR_INVALID_ARG, "num_pages must be >= 0");
+  if (grid < 1 || grid > 65535) return fail(DSA_ERR_INVALID_ARG, "grid %d not in [1, 65535]", grid);
+  if (rows && !aligned(rows, 4)) return fail(DSA_ERR_INVALID_ARG, "rows must be 4-byte aligned");
+  if (num_pages == 0) return DSA_OK;
+  dsa::ProbeArgs a;
+  a.base = static_cast<const uint8_t*>(base);
+  a.row_bytes = row_bytes;
+  a.offset = offset;
+  a.bytes_per_page = bytes_per_page;
+  a.rows = rows;
+  a.num_pages = num_pages;
+  a.sink = sink;
+  a.grid = grid;
+  return hip_status(dsa::launch_probe_read(a, static_cast<hipStream_t>(stream)),
+                    "dsa_probe_read launch");
+}
+
+dsa_status dsa_device_status(uint32_t* status, int32_t clear, void* stream) {
+  g_err[0] = 0;
+  if (!status) return fail(DSA_ERR_INVALID_ARG, "status is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* word;
+  dsa_status st = status_word(s, &word);
+  if (st != DSA_OK) return st;
+  if ((st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize")) != DSA_OK) return st;
+  if ((st = hip_status(hipMemcpy(status, word, sizeof(uint32_t), hipMemcpyDeviceToHost),
+                       "reading the status word")) != DSA_OK)
+    return st;
+  if (clear) {
+    static const uint32_t zero = 0;
+    if ((st = hip_status(hipMemcpy(word, &zero, sizeof(uint32_t), hipMemcpyHostToDevice),
+                         "clearing the status word")) != DSA_OK)
+      return st;
+  }
+  return DSA_OK;
+}
 
 dsa_status dsa_kv_layout_init(dsa_kv_layout* out, int32_t ikey_format, int32_t latent_format,
                               int32_t block_size, int64_t num_blocks, float latent_tensor_scale) {
@@ -262,6 +362,8 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   if (hist && !aligned(hist, 4)) return fail(DSA_ERR_INVALID_ARG, "hist must be 4-byte aligned");
   if (batch->num_rows == 0) return DSA_OK;
   dsa::IndexerArgs a;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = status_word(s, &a.status)) != DSA_OK) return st;
   a.pool = pool_view(kv, pool);
   a.batch = batch_view(batch);
   a.q = q_idx;
@@ -269,7 +371,6 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   a.scores = scores;
   a.ld = ld_scores;
   a.hist = hist;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ)
     return hip_status(dsa::launch_indexer_decode(a, kv->ikey_format, batch->max_rows_per_seq,
                                                  batch->max_context, s),
@@ -310,6 +411,9 @@ dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-aligned");
   dsa::TopkArgs a = {};
+  uint32_t* status;
+  if ((st = status_word(static_cast<hipStream_t>(stream), &status)) != DSA_OK) return st;
+  a.status = status;
   a.batch = batch_view(batch);
   a.scores = scores;
   a.ld = ld_scores;

@@ -25,6 +25,7 @@ struct IndexerArgs {
   uint32_t* hist;    // [R][2048] or null
   int32_t tiles_per_seq;  // row tiles per sequence (1 on the decode path)
   int32_t pages_per_wave; // multi-row scorer: key pages per wave (a multiple of 4)
+  uint32_t* status;       // the device status word (DSA_DEVERR_* bits)
 };
 
 // Decode / speculative decode scorer: grid (chunks, num_seqs).
@@ -54,6 +55,7 @@ struct TopkArgs {
   int64_t cand_ld;
   int32_t num_slices;
   int32_t vec_ok;       // scores rows are 16-byte aligned
+  const uint32_t* status;  // the device status word: a row-count violation poisons the select
 };
 size_t topk_workspace_bytes(int32_t num_rows, int64_t max_context);
 hipError_t launch_topk(const TopkArgs& a, int64_t max_context, void* workspace, hipStream_t s);
@@ -80,6 +82,7 @@ struct MlaArgs {
   int32_t split_slots;      // partial slots per row (nsplit, or shards x nsplit across shards)
   int32_t out_direct;       // one split, no partials: the attention writes out and lse itself
   int32_t nt_partials;      // store the partials non-temporally (a large set)
+  uint32_t* status;         // the device status word (DSA_DEVERR_* bits), or null
 };
 int mla_num_splits(int32_t num_rows, int32_t k, bool invariant);
 size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant);
@@ -99,6 +102,20 @@ hipError_t launch_indexer_front(const PoolView& pool, uint8_t* base, int ikey_fm
                                 const int64_t* slot, const uint16_t* ikey, int32_t num_rows,
                                 const uint16_t* q, const float* w, uint8_t* qo, float* wo,
                                 hipStream_t s);
+
+// Read-bandwidth probe (measurement only): page i is bytes_per_page bytes at
+// base + (rows ? rows[i] : i) * row_bytes + offset.
+constexpr int kProbeMaxPieces = 576;  // 16-byte pieces per page (9,216 bytes)
+struct ProbeArgs {
+  const uint8_t* base;
+  int64_t row_bytes, offset;
+  int32_t bytes_per_page;
+  const int32_t* rows;
+  int64_t num_pages;
+  uint32_t* sink;  // [grid] one word per workgroup
+  int32_t grid;
+};
+hipError_t launch_probe_read(const ProbeArgs& a, hipStream_t s);
 
 // Decode context parallelism emulated on one GPU: shard lists and the exact merge.
 size_t dcp_mailbox_bytes(int32_t num_rows, int32_t k, int32_t num_shards);

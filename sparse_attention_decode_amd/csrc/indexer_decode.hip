@@ -159,7 +159,11 @@ void indexer_kernel(IndexerArgs a) {
   const int g = lane >> 4, c = lane & 15;
 
   const int r0 = __builtin_amdgcn_readfirstlane(a.batch.seq_row_start[seq] + tile * R);
-  const int nr = __builtin_amdgcn_readfirstlane(min(R, a.batch.seq_row_start[seq + 1] - r0));
+  const int rows_left = __builtin_amdgcn_readfirstlane(a.batch.seq_row_start[seq + 1] - r0);
+  const int nr = min(R, rows_left);
+  // rows past the sequence's last tile are never scored: a broken max_rows_per_seq
+  if (rows_left > R && tile == a.tiles_per_seq - 1 && blockIdx.x == 0 && tid == 0)
+    atomicOr(a.status, DSA_DEVERR_ROWS_PER_SEQ);
   if (nr <= 0) return;
   const int ppw = a.pages_per_wave;  // <= 64: one block-table entry per lane
   const int blk0 = blockIdx.x * kWaves * ppw;
@@ -202,7 +206,11 @@ void indexer_kernel(IndexerArgs a) {
   }
   // lane j: pool row of this wave's page j, or -1 where that page does not exist
   const int64_t pool_rows = a.pool.tokens / kBlock;
-  const int btv = (lane < ppw && my_blk < nblk && bt_raw >= 0 && bt_raw < pool_rows) ? bt_raw : -1;
+  const bool page_exists = lane < ppw && my_blk < nblk;
+  const int btv = (page_exists && bt_raw >= 0 && bt_raw < pool_rows) ? bt_raw : -1;
+  // a visible block outside the pool: its tokens score 0 (zero records), and the fact is recorded
+  if (__builtin_amdgcn_readfirstlane(__ballot(page_exists && btv < 0) != 0) && lane == 0)
+    atomicOr(a.status, DSA_DEVERR_BLOCK_ID);
   auto page_of = [&](int i) { return blk0 + wave + kWaves * i; };
   const int row_bytes = (int)a.pool.row_bytes;
   auto page_rsrc = [&](int i) {

@@ -334,9 +334,15 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       const int v = *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(prow) +
                                                       (uint32_t)(4 * jc));  // scalar base
       ph = (in && v < a.pool.tokens) ? v : -1;
+      if (in && v >= a.pool.tokens && a.status) atomicOr(a.status, DSA_DEVERR_POOL_ROW);
     } else if (in) {
       const int s = idx[jj];
-      ph = (s >= 0 && s < nvis) ? bt[s / kBlock] * kBlock + (s % kBlock) : -1;
+      if (s >= 0 && s < nvis) {
+        const int b = bt[s / kBlock];
+        const bool ok = b >= 0 && (int64_t)b * kBlock < a.pool.tokens;
+        ph = ok ? b * kBlock + (s % kBlock) : -1;
+        if (!ok && a.status) atomicOr(a.status, DSA_DEVERR_BLOCK_ID);
+      }
     }
     return ph;
   };

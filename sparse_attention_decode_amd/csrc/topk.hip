@@ -259,6 +259,15 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
   auto phys_of = [&](int s) { return bt[s / kBlock] * kBlock + (s % kBlock); };
 
   uint32_t* hist_row = a.hist_in + (int64_t)row * kBins;
+  if (*a.status & DSA_DEVERR_ROWS_PER_SEQ) {  // some scorer skipped rows: nothing is selected
+    for (int i = tid; i < k; i += kResolveThreads) {
+      out[i] = -1;
+      if (phys) phys[i] = -1;
+    }
+    for (int i = tid; i < kBins; i += kResolveThreads) hist_row[i] = 0;
+    if (tid == 0) a.count[row] = -1;
+    return;
+  }
   if (n <= k) {  // every visible token is selected
     for (int i = tid; i < k; i += kResolveThreads) {
       out[i] = i < n ? i : -1;
