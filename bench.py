@@ -193,7 +193,7 @@ def read_ceiling(wls, devs, kvs, reps: int = 10):
     rotating over the same batches as the timed steps; (b) a contiguous read of as many bytes from
     the start of each pool.  Returns GB/s of each (event-timed, `reps` launches)."""
     import torch
-    import sparse_attention_decode_amd as sad
+    from sparse_attention_decode_amd._lib import dsa_probe_read
     key_page = 64 * (132 if wls[0].ikey_fmt == 0 else 68)
     rows_list, npages = [], 0
     for wl, d in zip(wls, devs):
@@ -211,11 +211,11 @@ def read_ceiling(wls, devs, kvs, reps: int = 10):
         def run(j):
             kv, d = kvs[j], devs[j]
             if name == "pages":
-                sad.dsa_probe_read(d["pool"], kv.row_bytes, kv.ikey_off, key_page, rows_list[j],
-                                   rows_list[j].numel(), sink)
+                dsa_probe_read(d["pool"], kv.row_bytes, kv.ikey_off, key_page, rows_list[j],
+                               rows_list[j].numel(), sink)
             else:
-                sad.dsa_probe_read(d["pool"], key_page, 0, key_page, None,
-                                   rows_list[j].numel(), sink)
+                dsa_probe_read(d["pool"], key_page, 0, key_page, None, rows_list[j].numel(),
+                               sink)
         for i in range(3):
             run(i % len(devs))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
