@@ -216,6 +216,24 @@ DSA_API dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool,
                               size_t workspace_bytes, void* stream);
 
 /*
+ * sparse_mla_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and results,
+ * bit for bit, but the split partials live in a static 64 MiB array the library holds in each
+ * device's memory until the process ends, so the call takes no workspace and allocates nothing.
+ * Arguments as sparse_mla_decode.  Limit: sparse_mla_workspace_bytes(num_rows, k, flags) must be
+ * at most 64 MiB (every batch of up to 135 rows at k = 2,048; up to 42 rows with
+ * DSA_BATCH_INVARIANT), else DSA_ERR_WORKSPACE, checked before anything is launched.  Nothing in
+ * the array has to start at zero.  All calls on one device share that array: calls that overlap in time on
+ * one device (other streams, other threads) race and must be ordered by the caller.  The stream
+ * must belong to the current device.
+ */
+DSA_API dsa_status sparse_mla_decode_noalloc(const dsa_kv_layout* kv, const void* pool,
+                                             const dsa_batch* batch, const uint16_t* q,
+                                             const int32_t* idx, const int32_t* phys, int32_t k,
+                                             float softmax_scale, uint16_t* out, float* lse,
+                                             void* stream);
+
+/*
  * The step before the path ("vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Low-latency decode:
  * a fused DSA decode path: the indexer query is quantised with the head weights folded in, and the
  * new token's index key and latent go into the KV cache, the latent write overlapping the

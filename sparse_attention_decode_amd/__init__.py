@@ -15,7 +15,7 @@ from ._lib import (DSAError, DeviceBatch, KVLayout, kv_layout, dsa_indexer_score
                    dsa_dcp_publish, dsa_dcp_merge, dsa_lse_combine, dsa_dcp_partials_bytes,
                    sparse_mla_decode_shard, MERGE_PACKED, MERGE_SCORES,
                    MERGE_GENERIC, MAX_SHARDS, dsa_device_status, DEVERR_ROWS_PER_SEQ,
-                   DEVERR_BLOCK_ID, DEVERR_POOL_ROW)
+                   DEVERR_BLOCK_ID, DEVERR_POOL_ROW, sparse_mla_decode_noalloc)
 from .layer import DSALayer
 
 __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_bytes",
@@ -25,4 +25,5 @@ __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scor
            "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_lse_combine",
            "dsa_dcp_partials_bytes", "sparse_mla_decode_shard",
            "MERGE_PACKED", "MERGE_SCORES", "MERGE_GENERIC", "MAX_SHARDS", "dsa_device_status",
-           "DEVERR_ROWS_PER_SEQ", "DEVERR_BLOCK_ID", "DEVERR_POOL_ROW"]
+           "DEVERR_ROWS_PER_SEQ", "DEVERR_BLOCK_ID", "DEVERR_POOL_ROW",
+           "sparse_mla_decode_noalloc"]

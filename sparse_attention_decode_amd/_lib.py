@@ -18,7 +18,8 @@ MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 # Every symbol include/dsa.h declares.
 EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
            "sparse_mla_workspace_bytes",
-           "sparse_mla_decode", "sparse_mla_prefill", "dsa_cache_append", "dsa_quantize_query",
+           "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_noalloc",
+           "dsa_cache_append", "dsa_quantize_query",
            "dsa_indexer_front",
            "dsa_dcp_mailbox_bytes", "dsa_dcp_publish", "dsa_dcp_merge", "dsa_dcp_partials_bytes",
            "sparse_mla_decode_shard", "dsa_lse_combine", "dsa_device_status", "dsa_probe_read", "dsa_status_string",
@@ -85,6 +86,9 @@ def lib():
             f.restype = i32
             f.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch), vp, vp, vp, i32,
                           f32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sparse_mla_decode_noalloc.restype = i32
+        L.sparse_mla_decode_noalloc.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch),
+                                                vp, vp, vp, i32, f32, vp, vp, vp]
         L.dsa_cache_append.restype = i32
         L.dsa_cache_append.argtypes = [ctypes.POINTER(KVLayout), vp, i32, vp, vp, vp, vp]
         L.dsa_quantize_query.restype = i32
@@ -204,6 +208,16 @@ def sparse_mla_prefill(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None,
                        stream=None, phys=None):
     _mla("sparse_mla_prefill", kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse,
          workspace, stream)
+
+
+def sparse_mla_decode_noalloc(kv, pool, batch, q, idx, k, softmax_scale, out, lse=None,
+                              stream=None, phys=None):
+    """sparse_mla_decode with its split partials in the library's static per-device scratch (no
+    workspace argument; nothing is allocated)."""
+    _check(lib().sparse_mla_decode_noalloc(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c),
+                                           _ptr(q), _ptr(idx), _ptr(phys), k, softmax_scale,
+                                           _ptr(out), _ptr(lse), _stream(stream)),
+           "sparse_mla_decode_noalloc")
 
 
 def dsa_cache_append(kv: KVLayout, pool, slot, index_key=None, latent=None, stream=None):

@@ -16,6 +16,12 @@
 // code never uses this name as an address: each device's address comes from hipGetSymbolAddress.
 static __device__ uint32_t dev_status;
 
+// Scratch of sparse_mla_decode_noalloc (its split partials): a fixed array in each device's
+// memory, held until the process ends.  As with the status word, host code never passes this
+// name to a kernel or a copy; it uses the address hipGetSymbolAddress gives for the device.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -73,6 +79,29 @@ dsa_status status_word(hipStream_t stream, uint32_t** out) {
         return fail(DSA_ERR_HIP, "hipGetSymbolAddress(status word): %s", hipGetErrorString(e));
       p = static_cast<uint32_t*>(addr);
       g_status[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DSA_OK;
+}
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Address of the current device's scratch array, looked up once per device (with that device
+// current) on the first sparse_mla_decode_noalloc call there.
+dsa_status scratch_address(hipStream_t stream, void** out) {
+  int dev;
+  dsa_status st = current_device(stream, &dev);
+  if (st != DSA_OK) return st;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_symbol_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
     }
   }
   *out = p;
@@ -187,7 +216,8 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
                       float softmax_scale,
                       uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, bool prefill, int32_t shard = -1,
-                      int32_t num_shards = 1, const int32_t* count = nullptr) {
+                      int32_t num_shards = 1, const int32_t* count = nullptr,
+                      bool noalloc = false) {
   dsa_status st = check_layout(kv, pool);
   if (st != DSA_OK) return st;
   if ((st = check_batch(batch)) != DSA_OK) return st;
@@ -233,6 +263,18 @@ dsa_status mla_common(const dsa_kv_layout* kv, const void* pool, const dsa_batch
   a.part_lse = nullptr;
   a.part_exp = nullptr;
   a.nt_partials = 0;
+  if (!a.out_direct && noalloc) {
+    // the split partials go to the device's static scratch; every split writes its whole slot
+    // before the combine reads it, so nothing there has to start at zero
+    const size_t need = partial_bytes(batch->num_rows, a.split_slots);
+    if (need > kNoallocScratchBytes)
+      return fail(DSA_ERR_WORKSPACE,
+                  "%d rows at top-k %d need %zu bytes of split partials; the static scratch "
+                  "holds %zu (use sparse_mla_decode with a workspace)",
+                  batch->num_rows, k, need, kNoallocScratchBytes);
+    if ((st = scratch_address(stream, &workspace)) != DSA_OK) return st;
+    workspace_bytes = kNoallocScratchBytes;
+  }
   if (!a.out_direct) {
     const size_t need = partial_bytes(batch->num_rows, a.split_slots);
     // 16 MB and more: the set would evict as dirty lines during the next step's key stream
@@ -440,6 +482,15 @@ dsa_status sparse_mla_decode(const dsa_kv_layout* kv, const void* pool, const ds
   g_err[0] = 0;
   return mla_common(kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+dsa_status sparse_mla_decode_noalloc(const dsa_kv_layout* kv, const void* pool,
+                                     const dsa_batch* batch, const uint16_t* q, const int32_t* idx,
+                                     const int32_t* phys, int32_t k, float softmax_scale,
+                                     uint16_t* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  return mla_common(kv, pool, batch, q, idx, phys, k, softmax_scale, out, lse, nullptr, 0,
+                    static_cast<hipStream_t>(stream), false, -1, 1, nullptr, true);
 }
 
 dsa_status sparse_mla_prefill(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
