@@ -134,6 +134,7 @@ typedef struct dsa_batch {
 #define DSA_DEVERR_ROWS_PER_SEQ 1u /* a sequence had more rows than dsa_batch.max_rows_per_seq */
 #define DSA_DEVERR_BLOCK_ID 2u     /* a block-table entry of a visible block was outside the pool */
 #define DSA_DEVERR_POOL_ROW 4u     /* a physical row given to the attention was past the pool */
+#define DSA_DEVERR_CAND_OVERFLOW 8u /* a row's candidate list outgrew its capacity (candidates path) */
 
 /* Fill *out (host) with the pool layout for the given formats (block_size must be 64).
  * Returns INVALID_ARG for a null pointer or bad value, UNSUPPORTED for another block size. */
@@ -182,6 +183,37 @@ DSA_API dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, con
                             int64_t ld_scores, uint32_t* hist, int32_t k, int32_t* idx,
                             int32_t* count, int32_t* phys, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Steps 1 and 2 without stored scores: the candidates path (page: a scorer and an exact top-k
+ * select in two kernels, §Low-latency decode: a fused DSA decode path).  The scores of a full row
+ * are never written; the select receives only the tokens that can still make the row's top-k.
+ *   dsa_indexer_candidates  scores a sample of each sequence (every S-th 64-token block, S a power
+ *       of two near sqrt(max_context / 2k), chosen by the library), takes the sample's exact
+ *       top-k per row (kept as the row's first candidates) and its k-th key T with the tie cutoff
+ *       I, then scores the other blocks and keeps each token whose key (the order-preserving image
+ *       of its score) is above T, or equal to T with an index below I.  Any other token is beaten
+ *       by k sample tokens, so the candidates contain the exact top-k.
+ *   dsa_topk_candidates     selects each row's top-k from its candidates: the same result as
+ *       dsa_topk on dense scores (idx ascending, -1 padded; count; phys as in dsa_topk).
+ * Both take the same batch, k and workspace (at least dsa_candidates_workspace_bytes(num_rows,
+ * batch->max_context, k) bytes, 16-byte aligned; nothing in it has to be initialised), and the
+ * second must follow the first on the stream.  Limits: max_context up to 8,388,608; k in
+ * [1, DSA_MAX_TOPK].  A row's candidate list holds 2 S (k + 64) + k entries (about twice what
+ * independent scores produce); a row whose candidates outgrow it (scores far above the sample's
+ * in the blocks that were not sampled) gets count = -1 and idx = phys = -1, and the status word
+ * gets DSA_DEVERR_CAND_OVERFLOW: rerun such rows on the dense path (dsa_indexer_scores +
+ * dsa_topk), which is exact for every input.  While DSA_DEVERR_ROWS_PER_SEQ is set,
+ * dsa_topk_candidates writes count = -1 for every row, as dsa_topk does.
+ */
+DSA_API size_t dsa_candidates_workspace_bytes(int32_t num_rows, int64_t max_context, int32_t k);
+DSA_API dsa_status dsa_indexer_candidates(const dsa_kv_layout* kv, const void* pool,
+                                          const dsa_batch* batch, const uint8_t* q_idx,
+                                          const float* w, int32_t k, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+DSA_API dsa_status dsa_topk_candidates(const dsa_kv_layout* kv, const dsa_batch* batch, int32_t k,
+                                       void* workspace, size_t workspace_bytes, int32_t* idx,
+                                       int32_t* count, int32_t* phys, void* stream);
 
 /* Workspace bytes sparse_mla_decode needs for num_rows rows and top-k k with dsa_batch.flags
  * `flags` (sparse_mla_prefill needs none unless flags has DSA_BATCH_INVARIANT: then this size). */

@@ -15,7 +15,9 @@ from ._lib import (DSAError, DeviceBatch, KVLayout, kv_layout, dsa_indexer_score
                    dsa_dcp_publish, dsa_dcp_merge, dsa_lse_combine, dsa_dcp_partials_bytes,
                    sparse_mla_decode_shard, MERGE_PACKED, MERGE_SCORES,
                    MERGE_GENERIC, MAX_SHARDS, dsa_device_status, DEVERR_ROWS_PER_SEQ,
-                   DEVERR_BLOCK_ID, DEVERR_POOL_ROW, sparse_mla_decode_noalloc)
+                   DEVERR_BLOCK_ID, DEVERR_POOL_ROW, sparse_mla_decode_noalloc,
+                   DEVERR_CAND_OVERFLOW, dsa_candidates_workspace_bytes, dsa_indexer_candidates,
+                   dsa_topk_candidates)
 from .layer import DSALayer
 
 __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_bytes",
@@ -26,4 +28,5 @@ __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scor
            "dsa_dcp_partials_bytes", "sparse_mla_decode_shard",
            "MERGE_PACKED", "MERGE_SCORES", "MERGE_GENERIC", "MAX_SHARDS", "dsa_device_status",
            "DEVERR_ROWS_PER_SEQ", "DEVERR_BLOCK_ID", "DEVERR_POOL_ROW",
-           "sparse_mla_decode_noalloc"]
+           "sparse_mla_decode_noalloc", "DEVERR_CAND_OVERFLOW", "dsa_candidates_workspace_bytes",
+           "dsa_indexer_candidates", "dsa_topk_candidates"]

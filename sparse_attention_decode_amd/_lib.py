@@ -17,6 +17,7 @@ MAX_TOPK, HIST_BINS, MAX_ROWS_PER_SEQ = 2048, 2048, 8
 
 # Every symbol include/dsa.h declares.
 EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes", "dsa_topk",
+           "dsa_candidates_workspace_bytes", "dsa_indexer_candidates", "dsa_topk_candidates",
            "sparse_mla_workspace_bytes",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_noalloc",
            "dsa_cache_append", "dsa_quantize_query",
@@ -26,7 +27,7 @@ EXPORTS = ("dsa_kv_layout_init", "dsa_indexer_scores", "dsa_topk_workspace_bytes
            "dsa_last_error")
 MERGE_PACKED, MERGE_SCORES, MERGE_GENERIC, MAX_SHARDS = 0, 1, 2, 8
 # bits of the device status word (include/dsa.h)
-DEVERR_ROWS_PER_SEQ, DEVERR_BLOCK_ID, DEVERR_POOL_ROW = 1, 2, 4
+DEVERR_ROWS_PER_SEQ, DEVERR_BLOCK_ID, DEVERR_POOL_ROW, DEVERR_CAND_OVERFLOW = 1, 2, 4, 8
 
 
 class DSAError(RuntimeError):
@@ -79,6 +80,14 @@ def lib():
         L.dsa_topk.restype = i32
         L.dsa_topk.argtypes = [ctypes.POINTER(KVLayout), ctypes.POINTER(Batch), vp, i64, vp, i32,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dsa_candidates_workspace_bytes.restype = ctypes.c_size_t
+        L.dsa_candidates_workspace_bytes.argtypes = [i32, i64, i32]
+        L.dsa_indexer_candidates.restype = i32
+        L.dsa_indexer_candidates.argtypes = [ctypes.POINTER(KVLayout), vp, ctypes.POINTER(Batch),
+                                             vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.dsa_topk_candidates.restype = i32
+        L.dsa_topk_candidates.argtypes = [ctypes.POINTER(KVLayout), ctypes.POINTER(Batch), i32, vp,
+                                          ctypes.c_size_t, vp, vp, vp, vp]
         L.sparse_mla_workspace_bytes.restype = ctypes.c_size_t
         L.sparse_mla_workspace_bytes.argtypes = [i32, i32, ctypes.c_uint32]
         for fn in ("sparse_mla_decode", "sparse_mla_prefill"):
@@ -185,6 +194,28 @@ def dsa_topk(kv: KVLayout | None, batch: DeviceBatch, scores, hist, k: int, idx,
     _check(lib().dsa_topk(ctypes.byref(kv) if kv is not None else None, ctypes.byref(batch.c),
                           _ptr(scores), scores.stride(0), _ptr(hist), k, _ptr(idx), _ptr(count),
                           _ptr(phys), _ptr(workspace), ws_bytes, _stream(stream)), "dsa_topk")
+
+
+def dsa_candidates_workspace_bytes(num_rows: int, max_context: int, k: int) -> int:
+    return int(lib().dsa_candidates_workspace_bytes(num_rows, max_context, k))
+
+
+def dsa_indexer_candidates(kv: KVLayout, pool, batch: DeviceBatch, q_idx, w, k: int, workspace,
+                           stream=None):
+    """Scores without storing them: the sample pass, its select and the candidate pass."""
+    _check(lib().dsa_indexer_candidates(ctypes.byref(kv), _ptr(pool), ctypes.byref(batch.c),
+                                        _ptr(q_idx), _ptr(w), k, _ptr(workspace),
+                                        _nbytes(workspace), _stream(stream)),
+           "dsa_indexer_candidates")
+
+
+def dsa_topk_candidates(kv: KVLayout | None, batch: DeviceBatch, k: int, workspace, idx, count,
+                        phys=None, stream=None):
+    """The exact top-k of each row from its candidates (after dsa_indexer_candidates)."""
+    _check(lib().dsa_topk_candidates(ctypes.byref(kv) if kv is not None else None,
+                                     ctypes.byref(batch.c), k, _ptr(workspace),
+                                     _nbytes(workspace), _ptr(idx), _ptr(count), _ptr(phys),
+                                     _stream(stream)), "dsa_topk_candidates")
 
 
 def sparse_mla_workspace_bytes(num_rows: int, k: int, flags: int = 0) -> int:

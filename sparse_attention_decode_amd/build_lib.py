@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["dsa_api.hip", "indexer_decode.hip", "topk.hip", "sparse_mla.hip", "cache_write.hip",
-           "dcp_merge.hip", "probe.hip"]
+           "dcp_merge.hip", "probe.hip", "candidates.hip"]
 # NaN inputs are outside the documented domain of every entry point, so min/max need not quiet
 # signalling NaNs (IEEE mode off): ReLU is one v_max instead of a canonicalize plus a max.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

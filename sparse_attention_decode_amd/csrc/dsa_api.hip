@@ -413,6 +413,11 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   a.scores = scores;
   a.ld = ld_scores;
   a.hist = hist;
+  a.sample_stride = 1;
+  a.cand = nullptr;
+  a.cand_count = nullptr;
+  a.floor = nullptr;
+  a.cand_cap = 0;
   if (batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ)
     return hip_status(dsa::launch_indexer_decode(a, kv->ikey_format, batch->max_rows_per_seq,
                                                  batch->max_context, s),
@@ -467,6 +472,159 @@ dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, const float
   return hip_status(dsa::launch_topk(a, batch->max_context, workspace,
                                      static_cast<hipStream_t>(stream)),
                     "topk launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Layout of the candidates path's workspace: the sample's dense scores, each row's candidate
+// list, its count and its floor.
+struct CandLayout {
+  int32_t S;
+  int64_t samp_ld, cap;
+  size_t off_samp, off_cand, off_count, off_floor, total;
+};
+
+constexpr int64_t kCandMaxContext = (int64_t)1 << 23;
+
+CandLayout cand_layout(int32_t num_rows, int64_t max_context, int32_t k) {
+  CandLayout c;
+  const int64_t nb = (max_context + 63) / 64;
+  // the largest power of two S <= 32 with S^2 <= N / (2k) rounded to the nearer power: the
+  // sample's N / S scores (4 bytes) and the about S k candidates (8 bytes) then cost alike
+  int32_t S = 1;
+  while (S < 32 && 2 * S <= nb && (int64_t)(2 * S) * (2 * S) * k <= max_context) S *= 2;
+  c.S = S;
+  c.samp_ld = (nb + S - 1) / S * 64;
+  const int64_t room = 2 * (int64_t)S * (k + 64) + k;
+  c.cap = std::max<int64_t>(k, std::min<int64_t>(align_up(max_context, 64), room));
+  const size_t R = (size_t)num_rows;
+  size_t off = 0;
+  c.off_samp = off;
+  off = align_up(off + R * c.samp_ld * sizeof(float), 256);
+  c.off_cand = off;
+  off = align_up(off + R * c.cap * 8, 256);
+  c.off_count = off;
+  off = align_up(off + R * sizeof(int32_t), 256);
+  c.off_floor = off;
+  off = align_up(off + R * 2 * sizeof(uint32_t), 256);
+  c.total = off;
+  return c;
+}
+
+dsa_status check_cand_call(const dsa_batch* batch, int32_t k, const void* workspace,
+                           size_t workspace_bytes, CandLayout* c) {
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
+  if (batch->max_context > kCandMaxContext)
+    return fail(DSA_ERR_UNSUPPORTED, "the candidates path is built for contexts up to %lld tokens",
+                (long long)kCandMaxContext);
+  *c = cand_layout(batch->num_rows, batch->max_context, k);
+  if (batch->num_rows == 0) return DSA_OK;
+  if (!workspace || workspace_bytes < c->total)
+    return fail(DSA_ERR_WORKSPACE, "candidates workspace of %zu bytes needed, %zu given", c->total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return DSA_OK;
+}
+
+dsa::CandArgs cand_args(const dsa_batch* batch, int32_t k, void* ws, const CandLayout& c) {
+  dsa::CandArgs a = {};
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  a.batch = batch_view(batch);
+  a.k = k;
+  a.sample_stride = c.S;
+  a.samp = reinterpret_cast<const float*>(base + c.off_samp);
+  a.samp_ld = c.samp_ld;
+  a.cand = reinterpret_cast<uint2*>(base + c.off_cand);
+  a.cand_count = reinterpret_cast<int32_t*>(base + c.off_count);
+  a.floor = reinterpret_cast<uint32_t*>(base + c.off_floor);
+  a.cand_cap = c.cap;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_candidates_workspace_bytes(int32_t num_rows, int64_t max_context, int32_t k) {
+  if (num_rows <= 0 || max_context <= 0 || max_context > kCandMaxContext || k < 1 ||
+      k > DSA_MAX_TOPK)
+    return 0;
+  return cand_layout(num_rows, max_context, k).total;
+}
+
+dsa_status dsa_indexer_candidates(const dsa_kv_layout* kv, const void* pool, const dsa_batch* batch,
+                                  const uint8_t* q_idx, const float* w, int32_t k, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_layout(kv, pool);
+  if (st != DSA_OK) return st;
+  if ((st = check_batch(batch)) != DSA_OK) return st;
+  if (!q_idx || !w) return fail(DSA_ERR_INVALID_ARG, "q_idx and w must be non-NULL");
+  if (!aligned(q_idx, 16) || !aligned(w, 4))
+    return fail(DSA_ERR_INVALID_ARG, "q_idx must be 16-byte and w 4-byte aligned");
+  CandLayout c;
+  if ((st = check_cand_call(batch, k, workspace, workspace_bytes, &c)) != DSA_OK) return st;
+  if (batch->num_rows == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* status;
+  if ((st = status_word(s, &status)) != DSA_OK) return st;
+  dsa::CandArgs ca = cand_args(batch, k, workspace, c);
+  ca.status = status;
+  dsa::IndexerArgs a = {};
+  a.pool = pool_view(kv, pool);
+  a.batch = batch_view(batch);
+  a.q = q_idx;
+  a.w = w;
+  a.hist = nullptr;
+  a.status = status;
+  a.sample_stride = c.S;
+  a.cand = ca.cand;
+  a.cand_count = ca.cand_count;
+  a.floor = ca.floor;
+  a.cand_cap = c.cap;
+  const bool decode = batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ;
+  auto score = [&](int mode) {
+    return decode ? dsa::launch_indexer_decode(a, kv->ikey_format, batch->max_rows_per_seq,
+                                               batch->max_context, s, mode)
+                  : dsa::launch_indexer_prefill(a, kv->ikey_format, batch->max_context,
+                                                batch->max_rows_per_seq, s, mode);
+  };
+  // the sample blocks, dense, in sample numbering
+  a.scores = const_cast<float*>(ca.samp);
+  a.ld = c.samp_ld;
+  if ((st = hip_status(score(dsa::kScoreSample), "sample scorer launch")) != DSA_OK) return st;
+  // the sample's top-k and floor
+  if ((st = hip_status(dsa::launch_cand_select(ca, 0, s), "sample select launch")) != DSA_OK)
+    return st;
+  // the other blocks, into the candidate lists
+  a.scores = nullptr;
+  a.ld = 0;
+  return hip_status(score(dsa::kScoreCand), "candidate scorer launch");
+}
+
+dsa_status dsa_topk_candidates(const dsa_kv_layout* kv, const dsa_batch* batch, int32_t k,
+                               void* workspace, size_t workspace_bytes, int32_t* idx,
+                               int32_t* count, int32_t* phys, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (!idx || !count) return fail(DSA_ERR_INVALID_ARG, "idx and count must be non-NULL");
+  if (phys) {
+    if (!kv) return fail(DSA_ERR_INVALID_ARG, "kv layout is required for phys rows");
+    if (kv->block_size != 64) return fail(DSA_ERR_UNSUPPORTED, "block_size must be 64");
+  }
+  CandLayout c;
+  if ((st = check_cand_call(batch, k, workspace, workspace_bytes, &c)) != DSA_OK) return st;
+  if (batch->num_rows == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dsa::CandArgs ca = cand_args(batch, k, workspace, c);
+  if ((st = status_word(s, &ca.status)) != DSA_OK) return st;
+  ca.idx = idx;
+  ca.count = count;
+  ca.phys = phys;
+  return hip_status(dsa::launch_cand_select(ca, 1, s), "candidate select launch");
 }
 
 size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k, uint32_t flags) {

@@ -26,14 +26,46 @@ struct IndexerArgs {
   int32_t tiles_per_seq;  // row tiles per sequence (1 on the decode path)
   int32_t pages_per_wave; // multi-row scorer: key pages per wave (a multiple of 4)
   uint32_t* status;       // the device status word (DSA_DEVERR_* bits)
+  // Candidates path (scores never stored in full).  The sample pass scores blocks 0, S, 2S, ...
+  // of each sequence into `scores` in sample numbering (sample token 64 j + t is token
+  // 64 S j + t); the candidate pass scores the other blocks and appends (order key, token) of
+  // each token at or above its row's floor to the row's candidate list.
+  int32_t sample_stride;   // S (>= 1)
+  uint2* cand;             // [R][cand_cap]
+  int32_t* cand_count;     // [R] entries appended so far (may exceed cand_cap: overflow)
+  const uint32_t* floor;   // [R][2]: key T and tie cutoff I: keep key > T, or key == T and token < I
+  int64_t cand_cap;
 };
+// Scorer modes: every block into dense scores; the sample blocks into dense sample scores; the
+// other blocks into candidate lists.
+enum { kScoreDense = 0, kScoreSample = 1, kScoreCand = 2 };
 
 // Decode / speculative decode scorer: grid (chunks, num_seqs).
 hipError_t launch_indexer_decode(const IndexerArgs& a, int ikey_fmt, int rows_per_seq,
-                                 int64_t max_context, hipStream_t s);
+                                 int64_t max_context, hipStream_t s, int mode = kScoreDense);
 // Prefill scorer (dense contraction of row tiles x key tiles; FP8 or MXFP4 keys).
 hipError_t launch_indexer_prefill(const IndexerArgs& a, int ikey_fmt, int64_t max_context,
-                                  int32_t max_rows_per_seq, hipStream_t s);
+                                  int32_t max_rows_per_seq, hipStream_t s, int mode = kScoreDense);
+
+// Candidate selects (one workgroup per row): SRC 0 reads a row's dense sample scores and leaves
+// its exact top-k as the row's first candidates plus the floor; SRC 1 selects the row's top-k
+// from its candidate list and writes idx / count / phys.
+struct CandArgs {
+  BatchView batch;
+  int32_t k;
+  int32_t sample_stride;
+  const float* samp;  // [R][samp_ld] sample scores (SRC 0)
+  int64_t samp_ld;
+  uint2* cand;        // [R][cand_cap]
+  int32_t* cand_count;
+  uint32_t* floor;    // [R][2]
+  int64_t cand_cap;
+  int32_t* idx;       // [R][k] (SRC 1)
+  int32_t* count;     // [R]
+  int32_t* phys;      // [R][k] or null
+  uint32_t* status;
+};
+hipError_t launch_cand_select(const CandArgs& a, int src, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 
 constexpr int kTopkSlice = 4096;   // scores per filter workgroup

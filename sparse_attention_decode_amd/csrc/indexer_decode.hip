@@ -128,9 +128,17 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu
 // (gfx9 counts loads and stores on one counter, and a mix makes every later wait a full drain).
 // NTH: threads per workgroup (the prefill tile with a histogram takes 8 waves, so that the one
 // workgroup its LDS allows per CU still puts two waves on each SIMD).
-template <int R, int KFMT, bool HIST, bool NT = false, int NTH = kThreads>
+// MODE: kScoreDense (every block, dense scores), kScoreSample (blocks 0, S, 2S, ..., dense
+// scores in sample numbering), kScoreCand (the other blocks; tokens at or above the row's floor
+// are staged in LDS and appended to the row's candidate list, one global atomic per row and
+// workgroup).
+template <int R, int KFMT, bool HIST, bool NT = false, int NTH = kThreads, int MODE = kScoreDense>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_kernel(IndexerArgs a) {
+  static_assert(!(HIST && MODE != kScoreDense), "the candidate path counts no histogram");
+  constexpr bool kCand = MODE == kScoreCand;
+  // candidates staged per row in LDS (more spill straight to the row's global list)
+  constexpr int kStage = !kCand ? 1 : (R <= 2 ? 512 : 256);
   constexpr int AUX = NT ? 2 : 0;  // cache policy of the key loads
   constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
@@ -151,6 +159,8 @@ void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? kHistWords : 1];
+  __shared__ uint2 s_cand[kCand ? R * kStage : 1];
+  __shared__ uint32_t s_ncand[kCand ? R : 1], s_cbase[kCand ? R : 1];
   // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
   const int seq = blockIdx.y / a.tiles_per_seq;
   const int tile = blockIdx.y % a.tiles_per_seq;
@@ -167,6 +177,13 @@ void indexer_kernel(IndexerArgs a) {
   if (nr <= 0) return;
   const int ppw = a.pages_per_wave;  // <= 64: one block-table entry per lane
   const int blk0 = blockIdx.x * kWaves * ppw;
+  // logical page lp of this launch -> block of the sequence
+  const int S = a.sample_stride;
+  auto map_block = [&](int lp) {
+    if (MODE == kScoreSample) return lp * S;
+    if (MODE == kScoreCand) return lp + lp / (S - 1) + 1;  // the blocks that are not multiples of S
+    return lp;
+  };
 
   // Loads that need only the sequence and the rows, issued together before the row positions are
   // read: the block-table entry of this wave's page `lane` (first, so the first page waits for it
@@ -174,7 +191,7 @@ void indexer_kernel(IndexerArgs a) {
   // their head weights (rows past nr repeat the last row; their results are never used).
   const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   const int my_blk = blk0 + wave + kWaves * lane;
-  const int bt_raw = bt[min((int64_t)my_blk, a.batch.ld_bt - 1)];
+  const int bt_raw = bt[min((int64_t)map_block(my_blk), a.batch.ld_bt - 1)];
   uint4 qv[kQPer];
   float wl[kWPer];
 #pragma unroll
@@ -193,13 +210,23 @@ void indexer_kernel(IndexerArgs a) {
   }
   asm volatile("" ::: "memory");  // not to be sunk below the early exit
   int pos[R];
+  uint32_t fT[kCand ? R : 1];
+  int fI[kCand ? R : 1];
   int L = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pos[r] = r < nr ? a.batch.row_pos[r0 + r] : -1;
     L = max(L, pos[r] + 1);
+    if constexpr (kCand) {
+      fT[r] = r < nr ? a.floor[2 * (r0 + r)] : 0xFFFFFFFFu;
+      fI[r] = r < nr ? (int)a.floor[2 * (r0 + r) + 1] : -1;
+    }
   }
-  const int nblk = (L + kBlock - 1) / kBlock;
+  // logical pages of this launch over the longest row's blocks
+  const int nb_seq = (L + kBlock - 1) / kBlock;
+  const int nblk = MODE == kScoreDense ? nb_seq
+                   : MODE == kScoreSample ? (nb_seq + S - 1) / S
+                                          : nb_seq - (nb_seq + S - 1) / S;
   if (blk0 >= nblk) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
@@ -239,6 +266,7 @@ void indexer_kernel(IndexerArgs a) {
   }
   if (HIST)
     for (int i = tid; i < kHistWords; i += NTH) s_hist[i] = 0;
+  if (kCand && tid < R) s_ncand[tid] = 0;
   lds_barrier();  // not a wait for the first page: the second is requested before that
 
   // Scores of the group of G pages starting at page i0 into sbuf (and the histogram).
@@ -250,7 +278,7 @@ void indexer_kernel(IndexerArgs a) {
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const float cur_scale = bscale[u & 1];
-      const int blk = page_of(i);
+      const int blk = map_block(page_of(i));
       // The rows' queries and weights come from LDS one row ahead of their use, so each row's
       // reads are in flight while the previous row is scored.  Not hoisted further: out of the
       // page loop they would hold 24 registers per row for the whole kernel.
@@ -302,6 +330,33 @@ void indexer_kernel(IndexerArgs a) {
         // would be sunk there and every page's key fragments would stay live until then
         asm volatile("" : "+v"(mine));
         sbuf[r][u] = mine;
+        if constexpr (kCand) {
+          const int tok = blk * kBlock + lane;
+          const uint32_t key = order_key(mine);
+          const bool keep = r < nr && tok <= pos[r] &&
+                            (key > fT[r] || (key == fT[r] && tok < fI[r]));
+          const uint64_t m = __ballot(keep);
+          if (m) {  // wave-uniform
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_ncand[r], (uint32_t)__popcll(m));
+            base = __builtin_amdgcn_readfirstlane(base);
+            const uint32_t p =
+                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (keep && p < (uint32_t)kStage) s_cand[r * kStage + p] = uint2{key, (uint32_t)tok};
+            const uint64_t spill = __ballot(keep && p >= (uint32_t)kStage);
+            if (spill) {  // the staging area is full: straight to the row's global list (rare)
+              uint32_t gb = 0;
+              if (lane == 0) gb = atomicAdd(&a.cand_count[r0 + r], (int)__popcll(spill));
+              gb = __builtin_amdgcn_readfirstlane(gb);
+              const uint32_t q =
+                  gb + __builtin_amdgcn_mbcnt_hi((uint32_t)(spill >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)spill, 0u));
+              if (keep && p >= (uint32_t)kStage && q < (uint64_t)a.cand_cap)
+                a.cand[(int64_t)(r0 + r) * a.cand_cap + q] = uint2{key, (uint32_t)tok};
+            }
+          }
+        }
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
         {
           const uint32_t bin = order_key(mine) >> 21;
@@ -321,19 +376,38 @@ void indexer_kernel(IndexerArgs a) {
   };
   // One coalesced 256-byte streaming store per (page, row) of the group starting at page i0.
   auto store_group = [&](int i0, const float (&sbuf)[R][G]) {
+    if constexpr (kCand) return;  // candidates were staged as they were scored
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
       if (i >= ppw || page_of(i) >= nblk) break;
-      const int s = page_of(i) * kBlock + lane;
+      const int lp = page_of(i);
+      const int s_tok = map_block(lp) * kBlock + lane;  // the token (visibility)
+      const int s_at = lp * kBlock + lane;               // its place in this launch's scores
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         // row offset kept scalar and computed here (hoisted, 16 rows of 64-bit VGPR addresses
         // would stay live through the whole page loop)
         int64_t off = (int64_t)(r0 + r) * a.ld;
         asm volatile("" : "+s"(off));
-        if (r < nr && s <= pos[r]) __builtin_nontemporal_store(sbuf[r][u], &a.scores[off + s]);
+        if (r < nr && s_tok <= pos[r]) __builtin_nontemporal_store(sbuf[r][u], &a.scores[off + s_at]);
       }
+    }
+  };
+  // Candidates staged in LDS go to the rows' global lists: one atomic per row reserves the
+  // places, then the whole workgroup copies.
+  auto flush_cand = [&]() {
+    __syncthreads();  // every wave's staged candidates are in LDS
+    if (tid < nr) {
+      const uint32_t n = min(s_ncand[tid], (uint32_t)kStage);
+      s_cbase[tid] = n ? (uint32_t)atomicAdd(&a.cand_count[r0 + tid], (int)n) : 0u;
+    }
+    __syncthreads();
+    for (int r = 0; r < nr; ++r) {
+      const uint32_t n = min(s_ncand[r], (uint32_t)kStage), base = s_cbase[r];
+      uint2* dst = a.cand + (int64_t)(r0 + r) * a.cand_cap;
+      for (uint32_t i = tid; i < n; i += NTH)
+        if (base + i < (uint64_t)a.cand_cap) dst[base + i] = s_cand[r * kStage + i];
     }
   };
   auto flush_hist = [&]() {
@@ -366,6 +440,7 @@ void indexer_kernel(IndexerArgs a) {
     }
     if (HIST) flush_hist();
   }
+  if constexpr (kCand) flush_cand();
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
@@ -373,10 +448,40 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// The sample and candidate passes of the candidates path (no histogram).  Decode rows stream
+// their keys past the caches (the path is for long contexts); a prefill tile keeps them cached
+// for the next row tile, and its candidate pass takes 8 waves (its staging area leaves room for
+// one workgroup per CU).
+template <int KFMT, int MODE>
+hipError_t launch_cand_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s) {
+  switch (rows) {
+#define DSA_CASE(R)                                                                               \
+  case R:                                                                                         \
+    hipLaunchKernelGGL((indexer_kernel<R, KFMT, false, true, kThreads, MODE>), grid,              \
+                       dim3(kThreads), 0, s, a);                                                  \
+    break;
+    DSA_CASE(1) DSA_CASE(2) DSA_CASE(3) DSA_CASE(4) DSA_CASE(5) DSA_CASE(6) DSA_CASE(7) DSA_CASE(8)
+#undef DSA_CASE
+    case kPrefillRows:
+      if (MODE == kScoreCand)
+        hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false, false, kPrefillThreads, MODE>),
+                           grid, dim3(kPrefillThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false, false, kThreads, MODE>),
+                           grid, dim3(kThreads), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // nt: stream the keys past the caches (decode with a histogram only).
 template <int KFMT>
 hipError_t launch_many_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream_t s,
-                            bool nt = false) {
+                            bool nt = false, int mode = kScoreDense) {
+  if (mode == kScoreSample) return launch_cand_rows<KFMT, kScoreSample>(a, rows, grid, s);
+  if (mode == kScoreCand) return launch_cand_rows<KFMT, kScoreCand>(a, rows, grid, s);
   switch (rows) {
 #define DSA_CASE(R)                                                                              \
   case R:                                                                                        \
@@ -413,11 +518,23 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+// Pages one launch visits per sequence of max_context tokens: every block, the sample blocks
+// (0, S, 2S, ...) or the others.
+int64_t launch_pages(int64_t max_context, int mode, int S) {
+  const int64_t nb = (max_context + kBlock - 1) / kBlock;
+  if (mode == kScoreSample) return (nb + S - 1) / S;
+  if (mode == kScoreCand) return nb - (nb + S - 1) / S;
+  return nb;
+}
+}  // namespace
+
 hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_per_seq,
-                                 int64_t max_context, hipStream_t s) {
+                                 int64_t max_context, hipStream_t s, int mode) {
   IndexerArgs a = a0;
   a.tiles_per_seq = 1;
-  const int64_t nblk = (max_context + kBlock - 1) / kBlock;
+  const int64_t nblk = launch_pages(max_context, mode, a.sample_stride);
+  if (nblk <= 0) return hipSuccess;
   // Workgroups, from the longest sequence: about 1024 for one or two rows (4 to 8 pages per
   // wave; with three workgroups resident per CU that is about 1.3 rounds, so the score stores of
   // the first round overlap the key reads of the second: measured faster than one round of 688
@@ -444,8 +561,9 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
   const int64_t key_bytes = a.batch.num_seqs * max_context *
                             (ikey_fmt == DSA_IKEY_FP8 ? DSA_INDEX_DIM + 4 : DSA_INDEX_DIM / 2 + 4);
   const bool nt = key_bytes >= ((int64_t)64 << 20);
-  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s, nt)
-                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s, nt);
+  return ikey_fmt == DSA_IKEY_FP8
+             ? launch_many_rows<DSA_IKEY_FP8>(a, rows_per_seq, grid, s, nt, mode)
+             : launch_many_rows<DSA_IKEY_MXFP4>(a, rows_per_seq, grid, s, nt, mode);
 }
 
 // Prefill: the rows of a sequence are cut into tiles of 16 (queries in LDS); each workgroup
@@ -453,13 +571,15 @@ hipError_t launch_indexer_decode(const IndexerArgs& a0, int ikey_fmt, int rows_p
 // workgroups in all.  Key pages
 // are re-read once per row tile, from L2 / the memory-side cache for a context that fits there.
 hipError_t launch_indexer_prefill(const IndexerArgs& a0, int ikey_fmt, int64_t max_context,
-                                  int32_t max_rows_per_seq, hipStream_t s) {
+                                  int32_t max_rows_per_seq, hipStream_t s, int mode) {
   IndexerArgs a = a0;
   constexpr int R = kPrefillRows;
-  // with a histogram the tile's workgroup has 8 waves (the same waves per CU as two 4-wave ones)
-  const int kWaves = (a.hist ? kPrefillThreads : kThreads) / kWave;
+  // with a histogram, or the candidate pass's staging area, the tile's workgroup has 8 waves (the
+  // same waves per CU as two 4-wave ones)
+  const int kWaves = (a.hist || mode == kScoreCand ? kPrefillThreads : kThreads) / kWave;
   a.tiles_per_seq = (max_rows_per_seq + R - 1) / R;
-  const int64_t nblk = (max_context + kBlock - 1) / kBlock;
+  const int64_t nblk = launch_pages(max_context, mode, a.sample_stride);
+  if (nblk <= 0) return hipSuccess;
   const int64_t gy = (int64_t)a.batch.num_seqs * a.tiles_per_seq;
   if (gy > 65535) return hipErrorInvalidValue;
   int64_t chunks = (2048 + gy - 1) / gy;
@@ -469,8 +589,8 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a0, int ikey_fmt, int64_t m
   if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
   a.pages_per_wave = (int32_t)ppw;
   dim3 grid((unsigned)((nblk + ppw * kWaves - 1) / (ppw * kWaves)), (unsigned)gy);
-  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s)
-                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, R, grid, s);
+  return ikey_fmt == DSA_IKEY_FP8 ? launch_many_rows<DSA_IKEY_FP8>(a, R, grid, s, false, mode)
+                                  : launch_many_rows<DSA_IKEY_MXFP4>(a, R, grid, s, false, mode);
 }
 
 }  // namespace dsa

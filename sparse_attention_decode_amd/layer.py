@@ -15,29 +15,39 @@ class DSALayer:
 
     def __init__(self, kv: L.KVLayout, batch: L.DeviceBatch, k: int = 2048,
                  softmax_scale: float = 1.0 / math.sqrt(192.0), prefill: bool = False,
-                 use_hist: bool | None = None, device="cuda"):
+                 use_hist: bool | None = None, device="cuda", candidates: bool = False):
         import torch
         self.kv, self.batch, self.k, self.softmax_scale = kv, batch, k, softmax_scale
         self.prefill = prefill
         R = batch.num_rows
         self.ld = (batch.c.max_context + 63) // 64 * 64
+        # candidates: scores are never stored; the scorer leaves each row's candidates in a
+        # workspace the select reads (dsa_indexer_candidates / dsa_topk_candidates)
+        self.candidates = bool(candidates)
+        if self.candidates:
+            nb = L.dsa_candidates_workspace_bytes(R, batch.c.max_context, k)
+            self.cand_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+            self.scores = self.hist = self.topk_ws = None
+            use_hist = False
         # By default the scorer counts the select's histogram on the decode path only: at prefill
         # the count inside the scorer (8-wave tiles, shared LDS bins) costs about what the
         # select's own pass saves (prefill-8192: -2%, prefill-2048: +5%).
         decode_path = batch.c.max_rows_per_seq <= L.MAX_ROWS_PER_SEQ
         self.use_hist = decode_path if use_hist is None else bool(use_hist)
-        self.scores = torch.empty((R, self.ld), dtype=torch.float32, device=device)
-        # zero on entry to the scorer; dsa_topk returns it to zero after consuming it
-        self.hist = (torch.zeros((R, L.HIST_BINS), dtype=torch.int32, device=device)
-                     if self.use_hist else None)
+        if not self.candidates:
+            self.scores = torch.empty((R, self.ld), dtype=torch.float32, device=device)
+            # zero on entry to the scorer; dsa_topk returns it to zero after consuming it
+            self.hist = (torch.zeros((R, L.HIST_BINS), dtype=torch.int32, device=device)
+                         if self.use_hist else None)
         self.idx = torch.empty((R, k), dtype=torch.int32, device=device)
         # pool rows of the selection, handed from the select to the attention
         self.phys = torch.empty((R, k), dtype=torch.int32, device=device)
         self.count = torch.empty((R,), dtype=torch.int32, device=device)
         self.out = torch.empty((R, L.MLA_HEADS, L.MLA_DV), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((R, L.MLA_HEADS), dtype=torch.float32, device=device)
-        tb = L.dsa_topk_workspace_bytes(R, batch.c.max_context)
-        self.topk_ws = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=device)
+        if not self.candidates:
+            tb = L.dsa_topk_workspace_bytes(R, batch.c.max_context)
+            self.topk_ws = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=device)
         flags = batch.c.flags
         nbytes = 0 if (prefill and not flags & L.BATCH_INVARIANT) else \
             L.sparse_mla_workspace_bytes(R, k, flags)
@@ -45,11 +55,20 @@ class DSALayer:
                                       device=device) if nbytes else None)
 
     def scores_step(self, pool, q_idx, w, stream=None):
-        L.dsa_indexer_scores(self.kv, pool, self.batch, q_idx, w, self.scores, self.hist, stream)
+        if self.candidates:
+            L.dsa_indexer_candidates(self.kv, pool, self.batch, q_idx, w, self.k, self.cand_ws,
+                                     stream)
+        else:
+            L.dsa_indexer_scores(self.kv, pool, self.batch, q_idx, w, self.scores, self.hist,
+                                 stream)
 
     def topk_step(self, stream=None, phys=True):
-        L.dsa_topk(self.kv, self.batch, self.scores, self.hist, self.k, self.idx, self.count,
-                   self.topk_ws, self.phys if phys else None, stream)
+        if self.candidates:
+            L.dsa_topk_candidates(self.kv, self.batch, self.k, self.cand_ws, self.idx,
+                                  self.count, self.phys if phys else None, stream)
+        else:
+            L.dsa_topk(self.kv, self.batch, self.scores, self.hist, self.k, self.idx, self.count,
+                       self.topk_ws, self.phys if phys else None, stream)
         self.phys_valid = bool(phys)
 
     def attention_step(self, pool, q, stream=None, use_phys=None):

@@ -13,16 +13,22 @@ import synth.device
 RTOL, ATOL = 2e-2, 2e-3  # bf16 outputs and fp32 log-sum-exp against the float64 oracle
 
 
-def run_gpu(wl: synth.Workload, use_hist=None, prefill=None, zero_qidx=False, phys=True, flags=0):
+def run_gpu(wl: synth.Workload, use_hist=None, prefill=None, zero_qidx=False, phys=True, flags=0,
+            candidates=False, pool_edit=None):
+    """Run the layer through the C ABI on workload wl.  candidates: scores are never stored (the
+    candidates path); pool_edit(pool, kv): a change made to the staged pool before the run."""
     kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
     d = synth.device.stage(wl, kv.as_dict())
     if zero_qidx:
         d["q_idx"].zero_()
+    if pool_edit is not None:
+        pool_edit(d["pool"], kv)
     batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
                             d["max_rows_per_seq"], d["max_context"], flags)
     if prefill is None:
         prefill = d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ
-    layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale, prefill=prefill, use_hist=use_hist)
+    layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale, prefill=prefill, use_hist=use_hist,
+                         candidates=candidates)
     layer.scores_step(d["pool"], d["q_idx"], d["w"])
     if phys:
         layer.phys.fill_(-7)
@@ -53,6 +59,7 @@ def check_rows(wl, layer, ref, rows, check_scores=True):
     idx = layer.idx[rows].cpu().numpy()
     cnt = layer.count[rows].cpu().numpy()
     assert ref["mism"] == 0, "inputs off the exact grid"
+    check_scores = check_scores and layer.scores is not None  # the candidates path stores none
     for i, r in enumerate(rows):
         p = int(wl.row_pos[r])
         if check_scores:

@@ -1,6 +1,7 @@
 """Parity of the HIP path with the oracle at the full sizes of the six measured workloads, in the
-launch configuration the benchmark times (scorer with its fused histogram, select emitting
-physical rows, attention reading them; prefill variants for the 8,192-row chunk).  The whole
+launch configurations the benchmark times (dense: scorer with its fused histogram, select
+emitting physical rows, attention reading them; candidates: scores never stored, the sample and
+candidate passes and the candidate select; prefill variants for the 8,192-row chunk).  The whole
 batch runs on the GPU; sampled rows are recomputed by the oracle one by one and compared element
 by element: scores and indices bit-exact, attention outputs within rtol 2e-2 / atol 2e-3."""
 import gc
@@ -27,8 +28,8 @@ def _sample_rows(wl, picks):
 def _check_sampled(wl, layer, rows):
     for r in rows:
         b = int(wl.row_seq[r])
-        print(f"[parity] {wl.name}: oracle row {r} (sequence {b}, position {wl.row_pos[r]})",
-              flush=True)
+        print(f"[parity] {wl.name}{' candidates' if layer.candidates else ''}: oracle row {r} "
+              f"(sequence {b}, position {wl.row_pos[r]})", flush=True)
         ref = oracle_seq(wl, b, rows=[r])
         check_rows(wl, layer, ref, [r])
 
@@ -46,41 +47,46 @@ def test_full_decode_1x8k():
     _check_sampled(wl, layer, [0])
 
 
-def test_full_decode_16x128k():
+@pytest.mark.parametrize("candidates", [False, True])
+def test_full_decode_16x128k(candidates):
     wl = synth.decode_config(1)
-    layer, _, _ = run_gpu(wl)
+    layer, _, _ = run_gpu(wl, candidates=candidates)
     _check_sampled(wl, layer, _sample_rows(wl, [0, 7, 15]))
 
 
-def test_full_specdec_16x6_1m():
+@pytest.mark.parametrize("candidates", [False, True])
+def test_full_specdec_16x6_1m(candidates):
     # 96 rows, six per sequence at positions L-6 .. L-1, sharing each sequence's 1M keys
     wl = synth.decode_config(2)
-    layer, _, _ = run_gpu(wl)
+    layer, _, _ = run_gpu(wl, candidates=candidates)
     assert not layer.prefill
     _check_sampled(wl, layer, _sample_rows(wl, [0, 5, 50, 95]))
 
 
-def test_full_prefill_8192_on_339968():
+@pytest.mark.parametrize("candidates", [False, True])
+def test_full_prefill_8192_on_339968(candidates):
     wl = synth.decode_config(3)
-    layer, _, _ = run_gpu(wl)
+    layer, _, _ = run_gpu(wl, candidates=candidates)
     assert layer.prefill
     _check_sampled(wl, layer, _sample_rows(wl, [0, 4095, 8191]))
     # every row has more than 2048 visible tokens: a full selection
     assert int(layer.count.min().item()) == wl.k
 
 
-def test_full_prefill_2048_on_150000():
+@pytest.mark.parametrize("candidates", [False, True])
+def test_full_prefill_2048_on_150000(candidates):
     # the short-append prefill: 2,048 rows after a 150,000-token prefix
     wl = synth.decode_config(5)
-    layer, _, _ = run_gpu(wl)
+    layer, _, _ = run_gpu(wl, candidates=candidates)
     assert layer.prefill
     _check_sampled(wl, layer, _sample_rows(wl, [0, 1023, 2047]))
     assert int(layer.count.min().item()) == wl.k
 
 
-def test_full_mixed_64_mxfp4_nvfp4():
+@pytest.mark.parametrize("candidates", [False, True])
+def test_full_mixed_64_mxfp4_nvfp4(candidates):
     wl = synth.decode_config(4)
-    layer, _, _ = run_gpu(wl)
+    layer, _, _ = run_gpu(wl, candidates=candidates)
     shortest = int(np.argmin(wl.row_pos))
     longest = int(np.argmax(wl.row_pos))
     _check_sampled(wl, layer, _sample_rows(wl, [shortest, longest, 17, 40]))
