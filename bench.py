@@ -26,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode layer query-tokens/s + achieved HBM TB/s (fraction of peak)"
+# workloads where the candidates path (scores never stored) measured faster than the dense one
+AUTO_CANDIDATES = (3,)
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0
@@ -339,6 +341,11 @@ def main():
                          "step, about 5%% of a decode-16x128K step)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the read-ceiling probe after the timed region")
+    ap.add_argument("--path", choices=["auto", "dense", "candidates"], default="auto",
+                    help="dense: scores stored, then dsa_topk; candidates: scores never stored "
+                         "(dsa_indexer_candidates + dsa_topk_candidates); auto: the faster one "
+                         "for the workload as measured (candidates for the 8,192-row prefill "
+                         "chunk, dense elsewhere)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--dcp", type=int, default=0,
@@ -376,6 +383,7 @@ def main():
 
     cfg = args.config
     reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2}[cfg]
+    use_cand = {"dense": False, "candidates": True}.get(args.path, cfg in AUTO_CANDIDATES)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
     wls, devs, layers, kvs = [], [], [], []
@@ -386,7 +394,8 @@ def main():
         batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
                                 d["max_rows_per_seq"], d["max_context"])
         layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale,
-                             prefill=d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ)
+                             prefill=d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ,
+                             candidates=use_cand)
         wls.append(wl)
         devs.append(d)
         layers.append(layer)
@@ -462,8 +471,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None if prefill else recorded_traffic(wl.name)
-    roof["kernel"] = "indexer_kernel (dsa_indexer_scores)"
+    roof["traffic"] = None if (prefill or use_cand) else recorded_traffic(wl.name)
+    roof["kernel"] = ("indexer_kernel sample + candidate passes with the sample select "
+                      "(dsa_indexer_candidates)" if use_cand else
+                      "indexer_kernel (dsa_indexer_scores)")
     roof["ms_per_launch"] = idx_ms
     roof["ms_per_launch_median"] = idx_samples[len(idx_samples) // 2]
     roof["timed_launches"] = len(evs)
@@ -485,7 +496,8 @@ def main():
                    "context": int(wl.seq_len.max()), "top_k": wl.k,
                    "index_keys": "fp8" if wl.ikey_fmt == 0 else "mxfp4",
                    "latent": "fp8" if wl.lat_fmt == 0 else "nvfp4", "block": 64,
-                   "batches_rotated": reps, "hip_graph": use_graph},
+                   "batches_rotated": reps, "hip_graph": use_graph,
+                   "path": "candidates" if use_cand else "dense"},
         "layer_hbm": {"algorithmic_bytes_per_step": total_b, "achieved_GBps": layer_gbps,
                       "frac_of_8TBps": layer_gbps / PEAK_HBM_GBPS},
         "roofline": roof,

@@ -416,6 +416,7 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   a.sample_stride = 1;
   a.cand = nullptr;
   a.cand_count = nullptr;
+  a.cand_max = nullptr;
   a.floor = nullptr;
   a.cand_cap = 0;
   if (batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ)
@@ -483,7 +484,7 @@ namespace {
 struct CandLayout {
   int32_t S;
   int64_t samp_ld, cap;
-  size_t off_samp, off_cand, off_count, off_floor, total;
+  size_t off_samp, off_cand, off_count, off_max, off_floor, total;
 };
 
 constexpr int64_t kCandMaxContext = (int64_t)1 << 23;
@@ -498,7 +499,7 @@ CandLayout cand_layout(int32_t num_rows, int64_t max_context, int32_t k) {
   c.S = S;
   c.samp_ld = (nb + S - 1) / S * 64;
   const int64_t room = 2 * (int64_t)S * (k + 64) + k;
-  c.cap = std::max<int64_t>(k, std::min<int64_t>(align_up(max_context, 64), room));
+  c.cap = align_up(std::max<int64_t>(k, std::min<int64_t>(align_up(max_context, 64), room)), 64);
   const size_t R = (size_t)num_rows;
   size_t off = 0;
   c.off_samp = off;
@@ -507,6 +508,8 @@ CandLayout cand_layout(int32_t num_rows, int64_t max_context, int32_t k) {
   off = align_up(off + R * c.cap * 8, 256);
   c.off_count = off;
   off = align_up(off + R * sizeof(int32_t), 256);
+  c.off_max = off;
+  off = align_up(off + R * sizeof(uint32_t), 256);
   c.off_floor = off;
   off = align_up(off + R * 2 * sizeof(uint32_t), 256);
   c.total = off;
@@ -538,6 +541,7 @@ dsa::CandArgs cand_args(const dsa_batch* batch, int32_t k, void* ws, const CandL
   a.samp_ld = c.samp_ld;
   a.cand = reinterpret_cast<uint2*>(base + c.off_cand);
   a.cand_count = reinterpret_cast<int32_t*>(base + c.off_count);
+  a.cand_max = reinterpret_cast<uint32_t*>(base + c.off_max);
   a.floor = reinterpret_cast<uint32_t*>(base + c.off_floor);
   a.cand_cap = c.cap;
   return a;
@@ -582,6 +586,7 @@ dsa_status dsa_indexer_candidates(const dsa_kv_layout* kv, const void* pool, con
   a.sample_stride = c.S;
   a.cand = ca.cand;
   a.cand_count = ca.cand_count;
+  a.cand_max = ca.cand_max;
   a.floor = ca.floor;
   a.cand_cap = c.cap;
   const bool decode = batch->max_rows_per_seq <= DSA_MAX_ROWS_PER_SEQ;

@@ -33,6 +33,7 @@ struct IndexerArgs {
   int32_t sample_stride;   // S (>= 1)
   uint2* cand;             // [R][cand_cap]
   int32_t* cand_count;     // [R] entries appended so far (may exceed cand_cap: overflow)
+  uint32_t* cand_max;      // [R] the largest key in the row's list
   const uint32_t* floor;   // [R][2]: key T and tie cutoff I: keep key > T, or key == T and token < I
   int64_t cand_cap;
 };
@@ -58,6 +59,7 @@ struct CandArgs {
   int64_t samp_ld;
   uint2* cand;        // [R][cand_cap]
   int32_t* cand_count;
+  uint32_t* cand_max; // [R]
   uint32_t* floor;    // [R][2]
   int64_t cand_cap;
   int32_t* idx;       // [R][k] (SRC 1)

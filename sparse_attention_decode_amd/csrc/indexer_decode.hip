@@ -137,8 +137,9 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_kernel(IndexerArgs a) {
   static_assert(!(HIST && MODE != kScoreDense), "the candidate path counts no histogram");
   constexpr bool kCand = MODE == kScoreCand;
-  // candidates staged per row in LDS (more spill straight to the row's global list)
-  constexpr int kStage = !kCand ? 1 : (R <= 2 ? 512 : 256);
+  // candidates staged in LDS per wave and row; a wave empties a row's slice into the row's global
+  // list when a page might not fit, and at its end
+  constexpr int kStage = !kCand ? 1 : (R <= 8 ? 128 : 64);
   constexpr int AUX = NT ? 2 : 0;  // cache policy of the key loads
   constexpr int G = R <= 2 ? kMaxPagesSmallR : (R <= 8 ? 4 : 2);  // pages per store group
   constexpr int NH = R <= 2 ? 2 : 1;  // histogram copies (lane parity): fewer same-address atomics
@@ -159,8 +160,7 @@ void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * DSA_INDEX_HEADS * kQRow];
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? kHistWords : 1];
-  __shared__ uint2 s_cand[kCand ? R * kStage : 1];
-  __shared__ uint32_t s_ncand[kCand ? R : 1], s_cbase[kCand ? R : 1];
+  __shared__ uint2 s_cand[kCand ? (NTH / kWave) * R * kStage : 1];
   // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
   const int seq = blockIdx.y / a.tiles_per_seq;
   const int tile = blockIdx.y % a.tiles_per_seq;
@@ -266,8 +266,32 @@ void indexer_kernel(IndexerArgs a) {
   }
   if (HIST)
     for (int i = tid; i < kHistWords; i += NTH) s_hist[i] = 0;
-  if (kCand && tid < R) s_ncand[tid] = 0;
   lds_barrier();  // not a wait for the first page: the second is requested before that
+
+  // Candidate slices of this wave (one per row) and their fill, wave-uniform: a wave appends
+  // without atomics, and its slices are read back only by itself (its LDS operations complete in
+  // order).  Emptying a slice: one global atomic reserves its place in the row's list, every
+  // lane copies, and the slice's largest key raises the row's maximum.
+  uint2* my_cand = s_cand + (kCand ? wave * R * kStage : 0);
+  uint32_t ncand[kCand ? R : 1];
+#pragma unroll
+  for (int r = 0; r < (kCand ? R : 1); ++r) ncand[r] = 0;
+  auto flush_row = [&](int r) {
+    uint32_t base = 0;
+    if (lane == 0) base = (uint32_t)atomicAdd(&a.cand_count[r0 + r], (int)ncand[r]);
+    base = __builtin_amdgcn_readfirstlane(base);
+    uint2* dst = a.cand + (int64_t)(r0 + r) * a.cand_cap;
+    uint32_t kmax = 0;
+    for (uint32_t i = lane; i < ncand[r]; i += kWave) {
+      const uint2 v = my_cand[r * kStage + i];
+      if (base + i < (uint64_t)a.cand_cap) dst[base + i] = v;
+      kmax = max(kmax, v.x);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
+    if (lane == 0) atomicMax(&a.cand_max[r0 + r], kmax);
+    ncand[r] = 0;
+  };
 
   // Scores of the group of G pages starting at page i0 into sbuf (and the histogram).
   auto score_group = [&](int i0, float (&sbuf)[R][G]) {
@@ -330,33 +354,6 @@ void indexer_kernel(IndexerArgs a) {
         // would be sunk there and every page's key fragments would stay live until then
         asm volatile("" : "+v"(mine));
         sbuf[r][u] = mine;
-        if constexpr (kCand) {
-          const int tok = blk * kBlock + lane;
-          const uint32_t key = order_key(mine);
-          const bool keep = r < nr && tok <= pos[r] &&
-                            (key > fT[r] || (key == fT[r] && tok < fI[r]));
-          const uint64_t m = __ballot(keep);
-          if (m) {  // wave-uniform
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_ncand[r], (uint32_t)__popcll(m));
-            base = __builtin_amdgcn_readfirstlane(base);
-            const uint32_t p =
-                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (keep && p < (uint32_t)kStage) s_cand[r * kStage + p] = uint2{key, (uint32_t)tok};
-            const uint64_t spill = __ballot(keep && p >= (uint32_t)kStage);
-            if (spill) {  // the staging area is full: straight to the row's global list (rare)
-              uint32_t gb = 0;
-              if (lane == 0) gb = atomicAdd(&a.cand_count[r0 + r], (int)__popcll(spill));
-              gb = __builtin_amdgcn_readfirstlane(gb);
-              const uint32_t q =
-                  gb + __builtin_amdgcn_mbcnt_hi((uint32_t)(spill >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)spill, 0u));
-              if (keep && p >= (uint32_t)kStage && q < (uint64_t)a.cand_cap)
-                a.cand[(int64_t)(r0 + r) * a.cand_cap + q] = uint2{key, (uint32_t)tok};
-            }
-          }
-        }
         if (HIST && r < nr && blk * kBlock + lane <= pos[r])
         {
           const uint32_t bin = order_key(mine) >> 21;
@@ -372,11 +369,30 @@ void indexer_kernel(IndexerArgs a) {
           }
         }
       }
+      if constexpr (kCand) {
+        // the page's tokens at or above their row's floor into this wave's slices, once every
+        // row of the page is scored (each row's scoring chain runs undisturbed)
+        const int tok = blk * kBlock + lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t key = order_key(sbuf[r][u]);
+          const bool keep = r < nr && tok <= pos[r] &&
+                            (key > fT[r] || (key == fT[r] && tok < fI[r]));
+          const uint64_t m = __ballot(keep);
+          const uint32_t add = (uint32_t)__popcll(m);
+          if (ncand[r] + add > (uint32_t)kStage) flush_row(r);  // the slice is full (rare)
+          const uint32_t p =
+              ncand[r] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (keep) my_cand[r * kStage + p] = uint2{key, (uint32_t)tok};
+          ncand[r] += add;
+        }
+      }
     }
   };
   // One coalesced 256-byte streaming store per (page, row) of the group starting at page i0.
   auto store_group = [&](int i0, const float (&sbuf)[R][G]) {
-    if constexpr (kCand) return;  // candidates were staged as they were scored
+    if constexpr (kCand) return;  // candidates were appended page by page
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
@@ -394,22 +410,7 @@ void indexer_kernel(IndexerArgs a) {
       }
     }
   };
-  // Candidates staged in LDS go to the rows' global lists: one atomic per row reserves the
-  // places, then the whole workgroup copies.
-  auto flush_cand = [&]() {
-    __syncthreads();  // every wave's staged candidates are in LDS
-    if (tid < nr) {
-      const uint32_t n = min(s_ncand[tid], (uint32_t)kStage);
-      s_cbase[tid] = n ? (uint32_t)atomicAdd(&a.cand_count[r0 + tid], (int)n) : 0u;
-    }
-    __syncthreads();
-    for (int r = 0; r < nr; ++r) {
-      const uint32_t n = min(s_ncand[r], (uint32_t)kStage), base = s_cbase[r];
-      uint2* dst = a.cand + (int64_t)(r0 + r) * a.cand_cap;
-      for (uint32_t i = tid; i < n; i += NTH)
-        if (base + i < (uint64_t)a.cand_cap) dst[base + i] = s_cand[r * kStage + i];
-    }
-  };
+
   auto flush_hist = [&]() {
     lds_barrier();  // every wave's LDS counts are in; its global stores need not be
     for (int i = tid; i < nr * kBins; i += NTH) {
@@ -440,7 +441,11 @@ void indexer_kernel(IndexerArgs a) {
     }
     if (HIST) flush_hist();
   }
-  if constexpr (kCand) flush_cand();
+  if constexpr (kCand) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ncand[r]) flush_row(r);
+  }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
