@@ -341,6 +341,9 @@ def main():
                          "step, about 5%% of a decode-16x128K step)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the read-ceiling probe after the timed region")
+    ap.add_argument("--plain-order", action="store_true",
+                    help="score a prefill chunk's row tiles in ascending order instead of the "
+                         "balanced 16-piece order (for comparison)")
     ap.add_argument("--path", choices=["auto", "dense", "candidates"], default="auto",
                     help="dense: scores stored, then dsa_topk; candidates: scores never stored "
                          "(dsa_indexer_candidates + dsa_topk_candidates); auto: the faster one "
@@ -382,7 +385,7 @@ def main():
         return
 
     cfg = args.config
-    reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2}[cfg]
+    reps = args.replicas or {0: 8, 1: 4, 2: 1, 3: 1, 4: 4, 5: 2, 6: 1}[cfg]
     use_cand = {"dense": False, "candidates": True}.get(args.path, cfg in AUTO_CANDIDATES)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
@@ -392,7 +395,8 @@ def main():
         kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
         d = synth.device.stage(wl, kv.as_dict())
         batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
-                                d["max_rows_per_seq"], d["max_context"])
+                                d["max_rows_per_seq"], d["max_context"],
+                                sad.BATCH_PLAIN_ORDER if args.plain_order else 0)
         layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale,
                              prefill=d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ,
                              candidates=use_cand)
@@ -464,7 +468,7 @@ def main():
     layer_gbps = total_b / (ms_step * 1e-3) / 1e9
     idx_gbps = idx_b / (idx_ms * 1e-3) / 1e9
     flops = indexer_flops(wl)
-    prefill = cfg in (3, 5)
+    prefill = cfg in (3, 5, 6)
     if prefill:
         roof = {"bound": "mfma", "achieved": flops / (idx_ms * 1e-3) / 1e12,
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
@@ -497,7 +501,8 @@ def main():
                    "index_keys": "fp8" if wl.ikey_fmt == 0 else "mxfp4",
                    "latent": "fp8" if wl.lat_fmt == 0 else "nvfp4", "block": 64,
                    "batches_rotated": reps, "hip_graph": use_graph,
-                   "path": "candidates" if use_cand else "dense"},
+                   "path": "candidates" if use_cand else "dense",
+                   "prefill_tile_order": "plain" if args.plain_order else "balanced"},
         "layer_hbm": {"algorithmic_bytes_per_step": total_b, "achieved_GBps": layer_gbps,
                       "frac_of_8TBps": layer_gbps / PEAK_HBM_GBPS},
         "roofline": roof,

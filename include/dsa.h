@@ -118,7 +118,7 @@ typedef struct dsa_batch {
   const int32_t* block_table;   /* [num_seqs * max_blocks_per_seq] pool row ids */
   const int32_t* seq_row_start; /* [num_seqs + 1] rows of sequence b: [start[b], start[b+1]) */
   const int32_t* row_pos;       /* [num_rows] */
-  uint32_t flags;               /* host: 0 or DSA_BATCH_INVARIANT (any other bit: INVALID_ARG) */
+  uint32_t flags;               /* host: DSA_BATCH_* bits below (any other bit: INVALID_ARG) */
 } dsa_batch;
 
 /* dsa_batch.flags: the attention splits each row's selected set into fixed 128-token parts, in
@@ -127,6 +127,13 @@ typedef struct dsa_batch {
  * Without it the split count follows the row count (faster; outputs then agree within rounding
  * between batches of different row counts).  Scores and the select are batch-invariant always. */
 #define DSA_BATCH_INVARIANT 1u
+
+/* dsa_batch.flags: score the row tiles of a prefill chunk in plain ascending order.  By default
+ * they are dispatched in the balanced order of token-sharded prefill (§Prefill: shard the attention
+ * by token, not by head): the chunk's row tiles are cut into 16 contiguous pieces and slot
+ * s = 0..7 takes pieces s and 15 - s, so that under the causal mask each stretch of dispatched
+ * work pairs a light piece with a heavy one.  Results are identical either way. */
+#define DSA_BATCH_PLAIN_ORDER 2u
 
 /* Bits of the device status word.  Once set, a bit stays set until dsa_device_status clears it;
  * while DSA_DEVERR_ROWS_PER_SEQ is set, every dsa_topk on that device writes count = -1 and

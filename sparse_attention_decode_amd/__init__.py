@@ -17,7 +17,7 @@ from ._lib import (DSAError, DeviceBatch, KVLayout, kv_layout, dsa_indexer_score
                    MERGE_GENERIC, MAX_SHARDS, dsa_device_status, DEVERR_ROWS_PER_SEQ,
                    DEVERR_BLOCK_ID, DEVERR_POOL_ROW, sparse_mla_decode_noalloc,
                    DEVERR_CAND_OVERFLOW, dsa_candidates_workspace_bytes, dsa_indexer_candidates,
-                   dsa_topk_candidates)
+                   dsa_topk_candidates, BATCH_PLAIN_ORDER)
 from .layer import DSALayer
 
 __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_bytes",
@@ -29,4 +29,4 @@ __all__ = ["DSAError", "DeviceBatch", "KVLayout", "kv_layout", "dsa_indexer_scor
            "MERGE_PACKED", "MERGE_SCORES", "MERGE_GENERIC", "MAX_SHARDS", "dsa_device_status",
            "DEVERR_ROWS_PER_SEQ", "DEVERR_BLOCK_ID", "DEVERR_POOL_ROW",
            "sparse_mla_decode_noalloc", "DEVERR_CAND_OVERFLOW", "dsa_candidates_workspace_bytes",
-           "dsa_indexer_candidates", "dsa_topk_candidates"]
+           "dsa_indexer_candidates", "dsa_topk_candidates", "BATCH_PLAIN_ORDER"]

@@ -57,6 +57,7 @@ class Batch(ctypes.Structure):
 
 
 BATCH_INVARIANT = 1  # dsa_batch.flags: attention split count from k alone (see include/dsa.h)
+BATCH_PLAIN_ORDER = 2  # dsa_batch.flags: prefill row tiles in ascending order, not balanced
 
 
 _lib = None

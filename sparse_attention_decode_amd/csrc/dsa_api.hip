@@ -145,7 +145,8 @@ dsa_status check_batch(const dsa_batch* b) {
     return fail(DSA_ERR_INVALID_ARG, "max_blocks_per_seq * 64 < max_context");
   if (!b->block_table || !b->seq_row_start || !b->row_pos)
     return fail(DSA_ERR_INVALID_ARG, "block_table, seq_row_start and row_pos must be non-NULL");
-  if (b->flags & ~DSA_BATCH_INVARIANT) return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
+  if (b->flags & ~(DSA_BATCH_INVARIANT | DSA_BATCH_PLAIN_ORDER))
+    return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
   return DSA_OK;
 }
 
@@ -413,6 +414,7 @@ dsa_status dsa_indexer_scores(const dsa_kv_layout* kv, const void* pool, const d
   a.scores = scores;
   a.ld = ld_scores;
   a.hist = hist;
+  a.plain_order = (batch->flags & DSA_BATCH_PLAIN_ORDER) != 0;
   a.sample_stride = 1;
   a.cand = nullptr;
   a.cand_count = nullptr;
@@ -583,6 +585,7 @@ dsa_status dsa_indexer_candidates(const dsa_kv_layout* kv, const void* pool, con
   a.w = w;
   a.hist = nullptr;
   a.status = status;
+  a.plain_order = (batch->flags & DSA_BATCH_PLAIN_ORDER) != 0;
   a.sample_stride = c.S;
   a.cand = ca.cand;
   a.cand_count = ca.cand_count;
@@ -814,7 +817,8 @@ dsa_status dsa_lse_combine(int32_t num_rows, int32_t k, int32_t num_shards, uint
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, 2048]", k);
   if (num_shards < 1 || num_shards > DSA_MAX_SHARDS)
     return fail(DSA_ERR_INVALID_ARG, "num_shards %d not in [1, %d]", num_shards, DSA_MAX_SHARDS);
-  if (flags & ~DSA_BATCH_INVARIANT) return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
+  if (flags & ~(DSA_BATCH_INVARIANT | DSA_BATCH_PLAIN_ORDER))
+    return fail(DSA_ERR_INVALID_ARG, "unknown batch flags");
   if (num_rows == 0) return DSA_OK;
   if (!out) return fail(DSA_ERR_INVALID_ARG, "out must be non-NULL");
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)))

@@ -24,6 +24,7 @@ struct IndexerArgs {
   int64_t ld;
   uint32_t* hist;    // [R][2048] or null
   int32_t tiles_per_seq;  // row tiles per sequence (1 on the decode path)
+  int32_t plain_order;    // prefill row tiles in ascending order instead of the balanced one
   int32_t pages_per_wave; // multi-row scorer: key pages per wave (a multiple of 4)
   uint32_t* status;       // the device status word (DSA_DEVERR_* bits)
   // Candidates path (scores never stored in full).  The sample pass scores blocks 0, S, 2S, ...

@@ -119,6 +119,26 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu
   }
 }
 
+// Launch slot y (of T row tiles of a prefill chunk) -> row tile, in the balanced 16-piece order
+// of token-sharded prefill ("vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Prefill: shard the
+// attention by token, not by head): the tiles are cut into 16 contiguous pieces, piece p holding
+// tiles [p T / 16, (p + 1) T / 16), and slot s = 0..7 takes pieces s and 15 - s.  Under the causal
+// mask a tile's work grows with its position, so each slot, and so each stretch of dispatched
+// workgroups, holds a light and a heavy piece.  A bijection on [0, T).
+__device__ __forceinline__ int balanced_tile(int y, int T) {
+  auto start = [&](int p) { return (int)(((int64_t)p * T) / 16); };
+  int acc = 0;
+  for (int sl = 0; sl < 8; ++sl) {
+    const int p0 = sl, p1 = 15 - sl;
+    const int n0 = start(p0 + 1) - start(p0), n1 = start(p1 + 1) - start(p1);
+    if (y < acc + n0) return start(p0) + (y - acc);
+    acc += n0;
+    if (y < acc + n1) return start(p1) + (y - acc);
+    acc += n1;
+  }
+  return y;  // not reached for y < T
+}
+
 // One workgroup scores the R query rows of one sequence (decode: 1 row; speculative
 // verification: up to 8; prefill: a tile of 16 rows of the chunk) against a run of that
 // sequence's key pages (at most 64 per wave).  The rows' queries and head weights sit in LDS
@@ -161,9 +181,11 @@ void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) float s_w[R * DSA_INDEX_HEADS];
   __shared__ uint32_t s_hist[HIST ? kHistWords : 1];
   __shared__ uint2 s_cand[kCand ? (NTH / kWave) * R * kStage : 1];
-  // blockIdx.y = (sequence, tile of R consecutive rows of that sequence)
+  // blockIdx.y = (sequence, tile of R consecutive rows of that sequence), the tiles in the
+  // balanced order unless the plain one is asked for
   const int seq = blockIdx.y / a.tiles_per_seq;
-  const int tile = blockIdx.y % a.tiles_per_seq;
+  const int tile = a.plain_order ? blockIdx.y % a.tiles_per_seq
+                                 : balanced_tile(blockIdx.y % a.tiles_per_seq, a.tiles_per_seq);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;

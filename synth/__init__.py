@@ -283,7 +283,7 @@ def decode_config(i: int, seed: int | None = None, replica: int = 0) -> Workload
     """The layer shapes this project measures: 0 decode 8K, 1 batched decode 16 x 128K,
     2 speculative decode 16 x (1+5) at 1M, 3 chunked prefill 8192 on 339,968, 4 mixed-length
     64 x log-uniform[4K, 256K] with MXFP4 keys and NVFP4 latents, 5 short-append prefill
-    2048 on 150,000."""
+    2048 on 150,000, 6 the first 16,384-row chunk of a prompt (positions 0 .. 16,383)."""
     seed = (1000 + i + 7919 * replica) if seed is None else seed
     if i == 0:
         return Workload("decode-1x8K", seed, [8192], [0], [8191])
@@ -303,6 +303,11 @@ def decode_config(i: int, seed: int | None = None, replica: int = 0) -> Workload
         P, T = 150000, 2048
         return Workload("prefill-2048-on-150000", seed, [P + T], [0] * T,
                         [P + t for t in range(T)])
+    if i == 6:
+        # the first chunk of a prompt: rows at every position from 0, so the causal work of a row
+        # grows along the chunk
+        T = 16384
+        return Workload("prefill-16384-from-0", seed, [T], [0] * T, list(range(T)))
     if i == 4:
         g = np.random.Generator(np.random.PCG64(seed + 1))
         Ls = np.floor(np.exp(g.uniform(math.log(4096), math.log(262144), 64))).astype(np.int64)

@@ -123,7 +123,7 @@ def test_batch_flags():
     kv = sad.kv_layout(sad.IKEY_FP8, sad.LATENT_FP8, 10)
     pool = ctypes.c_void_p(0x100000)
     p = ctypes.c_void_p(0x2000)
-    bad = _fake_batch(flags=2)
+    bad = _fake_batch(flags=4)  # bits 0 and 1 are DSA_BATCH_INVARIANT and DSA_BATCH_PLAIN_ORDER
     assert lib.dsa_indexer_scores(ctypes.byref(kv), pool, ctypes.byref(bad), p, p, p, 128, None,
                                   None) == L.DSA_ERR_INVALID_ARG
     assert lib.sparse_mla_decode(ctypes.byref(kv), pool, ctypes.byref(bad), p, p, p, 2048, 0.1,
@@ -226,7 +226,7 @@ def test_dcp_entry_points_validate_before_launch():
     assert pb == 4 * 2 * 32 * 96 * (512 * 2 + 8)
     assert lib.dsa_dcp_partials_bytes(4, 2048, 9, 0) == 0
     assert lib.dsa_lse_combine(4, 2048, 0, 0, mb, pb, p, None, None) == bad
-    assert lib.dsa_lse_combine(4, 2048, 2, 2, mb, pb, p, None, None) == bad
+    assert lib.dsa_lse_combine(4, 2048, 2, 4, mb, pb, p, None, None) == bad
     assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb - 1, p, None, None) == ws
     assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb, ctypes.c_void_p(0x2008), None, None) == bad
     assert lib.dsa_lse_combine(4, 2048, 2, 0, mb, pb, None, None, None) == bad

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_attention_decode_amd as sad
 import synth
 from gpu_harness import check_rows, oracle_seq, run_gpu
 
@@ -90,3 +91,15 @@ def test_full_mixed_64_mxfp4_nvfp4(candidates):
     shortest = int(np.argmin(wl.row_pos))
     longest = int(np.argmax(wl.row_pos))
     _check_sampled(wl, layer, _sample_rows(wl, [shortest, longest, 17, 40]))
+
+
+@pytest.mark.parametrize("plain", [False, True])
+def test_full_prefill_16384_from_0(plain):
+    # the first chunk of a prompt, its row tiles scored in the balanced 16-piece order or in plain
+    # ascending order: the same results either way, against the oracle on sampled rows
+    wl = synth.decode_config(6)
+    layer, _, _ = run_gpu(wl, flags=sad.BATCH_PLAIN_ORDER if plain else 0)
+    assert layer.prefill
+    _check_sampled(wl, layer, _sample_rows(wl, [0, 1, 2047, 2048, 9000, 16383]))
+    counts = layer.count.cpu().numpy()
+    assert np.array_equal(counts, np.minimum(wl.k, wl.row_pos + 1))
