@@ -227,8 +227,8 @@ DSA_API dsa_status dsa_topk_candidates(const dsa_kv_layout* kv, const dsa_batch*
 DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k, uint32_t flags);
 
 /*
- * Step 3 — exact MLA attention over the selected latents (page: every query head attends
- * exactly over only the selected tokens; the latent is shared by all heads).  For row r and
+ * Step 3 — exact MLA attention over the selected latents (page: attention is exact but limited
+ * to the chosen tokens, for all heads; the latent is shared by all heads).  For row r and
  * head h, over j in idx[r][0..k) with idx >= 0:
  *   c_j = dequantised latent of token idx[r][j] (FP8 code * token scale, or NVFP4)
  *   logit_j = softmax_scale * q[r,h] . c_j ;  p = softmax(logit)
@@ -236,7 +236,7 @@ DSA_API size_t sparse_mla_workspace_bytes(int32_t num_rows, int32_t k, uint32_t 
  *   q    [num_rows][96][576] bf16;  idx [num_rows][k] from dsa_topk
  *   phys [num_rows][k] pool rows of idx from dsa_topk, or NULL (then idx is translated through
  *        the block table here).  Passing the rows the select already emitted saves a dependent
- *        lookup per token (page: the select emits the physical KV rows the attention reads).
+ *        lookup per token (page: the select hands the attention pool rows, not logical indices).
  *   out  [num_rows][96][512] bf16 output;  lse [num_rows][96] fp32 output or NULL
  *   workspace: device scratch of at least sparse_mla_workspace_bytes(num_rows, k) bytes
  * A row with no selected token gets out = 0 and lse = -inf.  Latent token scales (FP8) and the
@@ -274,9 +274,9 @@ DSA_API dsa_status sparse_mla_decode_noalloc(const dsa_kv_layout* kv, const void
 
 /*
  * The step before the path ("vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Low-latency decode:
- * a fused DSA decode path: the indexer query is quantised with the head weights folded in, and the
- * new token's index key and latent go into the KV cache, the latent write overlapping the
- * indexer).  Rounding is to the nearest code, ties to the even code, saturating at the format's
+ * a fused DSA decode path: the indexer query is quantised with the head weights merged into its
+ * scale, and the new token's index key and latent go into the KV cache, the latent write
+ * overlapping the indexer).  Rounding is to the nearest code, ties to the even code, saturating at the format's
  * largest finite value; inputs must be finite.  The codes are exact functions of the bf16 inputs.
  *
  * dsa_cache_append — quantise num_tokens new tokens into their pool rows (formats as in

@@ -206,7 +206,7 @@ void orc_dequant_latent_nvfp4(int D, const uint8_t* packed, const uint8_t* bscal
 
 /*
  * Exact MLA attention of one query row over the selected latents ([K31] "Sparse Attention in
- * K3.1 Pro": every query head attends exactly over only the selected tokens; the latent is
+ * K3.1 Pro": attention is exact, restricted to the chosen tokens, for all heads alike; the latent is
  * shared by all heads).  For each head h:
  *   logit_j = softmax_scale * sum_{d<Dqk} q[h,d] * c[j,d]
  *   p_j     = exp(logit_j - max) / sum_j exp(logit_j - max)

@@ -3,9 +3,8 @@
 // Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Sparse Attention in K3.1 Pro (every
 // earlier token is scored for each query by 32 light heads over one FP8 key of 132 bytes with its
 // scale; long-context decode is bound by memory bandwidth); §AMD / Quantization: Native MXFP4
-// indexer (68-byte MXFP4 keys scored on FP4 matrix instructions with FP32 accumulation and a
-// weighted reduction across heads; keys reused across the query rows of a speculative
-// verification step).  Scoring rule (DeepSeek-V3.2 lightning indexer, which the page defers to):
+// indexer (68-byte MXFP4 keys, scored with the matrix cores in FP4 and summed in fp32 over the
+// weighted heads; one read of the keys serves every query row of a speculative step).  Scoring rule (DeepSeek-V3.2 lightning indexer, which the page defers to):
 //     score[r,s] = sum_h w[r,h] * ReLU(scale_s * q[r,h] . k[s])
 // computed here as scale_s * sum_h w[r,h] * ReLU(q[r,h] . k[s]) (scale_s > 0).
 //

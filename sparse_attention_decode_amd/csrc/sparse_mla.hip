@@ -1,8 +1,8 @@
 // Exact MLA attention over the selected latents (decode with split-K, and prefill).
 //
 // Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Sparse Attention in K3.1 Pro (MLA
-// runs exactly over only the selected tokens; every query head attends over those tokens'
-// latents); §Prefill: shard the attention by token (the latent is shared by all heads, so one
+// is computed exactly, but only over the chosen tokens, and all heads use the same chosen
+// tokens' latents); §Prefill: shard the attention by token (the latent is shared by all heads, so one
 // workgroup serves all 96 heads of a row and reads each latent once); §AMD / Prefill (one
 // workgroup per query row across the heads, reading the selected tokens straight from the FP8
 // cache); §A KV cache for three kinds of state (FP8 or NVFP4 latents).

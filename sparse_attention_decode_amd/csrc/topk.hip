@@ -2,7 +2,7 @@
 //
 // Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Sparse Attention in K3.1 Pro (keep
 // the 2,048 highest-scoring tokens); §Low-latency decode (an exact top-k select that emits the
-// physical KV rows the attention reads); §An exact top-k merge (a radix select); §AMD /
+// pool rows, which the attention then gathers); §An exact top-k merge (a radix select); §AMD /
 // Communication (a consistent tie rule).  Tie rule used here: the lower token index wins; -0 and
 // +0 tie.
 //
