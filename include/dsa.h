@@ -83,7 +83,10 @@ enum {
  *                                                            low nibble of byte j)
  *                         block scales [bs][36] E4M3 (one per 16 elements) at latent_scale_off
  *                         value = E2M1 * block scale * latent_tensor_scale
- *   ikey_format FP8:      keys         [bs][128] E4M3        at ikey_off
+ *   ikey_format FP8:      keys         [bs][128] E4M3        at ikey_off, in the scorer's load
+ *                         order: byte b of slot t at 2048 (t / 16) + 1024 (b / 64)
+ *                         + 256 ((b / 16) % 4) + 16 (t % 16) + b % 16 (each 16-byte piece a
+ *                         64-lane load takes, one per lane, is then part of one 1 KB run)
  *                         key scale    [bs] fp32 (> 0)       at ikey_scale_off
  *   ikey_format MXFP4:    keys         [bs][64] packed E2M1  at ikey_off
  *                         block scales [bs][4] E8M0 (one per 32 elements) at ikey_scale_off

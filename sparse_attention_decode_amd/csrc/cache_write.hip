@@ -87,7 +87,11 @@ __device__ __forceinline__ void write_index_key(const CacheWriteArgs& a, int t, 
   if (IKFMT == DSA_IKEY_FP8) {
     const float sc = fp8_token_scale(group_max<64>(fmaxf(fabsf(x0), fabsf(x1))));
     const uint32_t c = enc_e4m3(x0 / sc) | (enc_e4m3(x1 / sc) << 8);
-    reinterpret_cast<uint16_t*>(row + a.ikey_off + s * DSA_INDEX_DIM)[lane] = (uint16_t)c;
+    // the page's load order: byte b of slot s at 2048 (s / 16) + 1024 (b / 64) + 256 ((b / 16) % 4)
+    // + 16 (s % 16) + b % 16; this lane's bytes are b = 2 lane, 2 lane + 1
+    const int64_t at = 2048 * (s >> 4) + 1024 * (lane >> 5) + 256 * ((lane >> 3) & 3) +
+                       16 * (s & 15) + 2 * (lane & 7);
+    *reinterpret_cast<uint16_t*>(row + a.ikey_off + at) = (uint16_t)c;
     if (lane == 0) reinterpret_cast<float*>(row + a.ikey_scale_off)[s] = sc;
   } else {
     // OCP MX block of 32 = 16 lanes: E8M0 exponent floor(log2 amax) - 2 (E2M1's top exponent)

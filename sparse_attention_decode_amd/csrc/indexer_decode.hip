@@ -40,6 +40,11 @@ struct KeyFrag {
 // page's first 16-token tile (tile nt adds nt * 16 tokens), and its scale: FP8, the scale of token
 // 16g + c, the one token whose score the lane produces; MXFP4, the E8M0 scale of token c's K
 // block g (tile nt adds nt * 64 bytes).
+// FP8 key pages are stored in load order: lane 16g + c of a wave needs bytes [16g, 16g + 16) and
+// [64 + 16g, 64 + 16g + 16) of token c of each tile (its two 16-byte pieces of the MFMA B
+// operand), and the pool puts piece (tile nt, half h) of all 64 lanes in one contiguous 1 KB run
+// at 2048 nt + 1024 h, lane-ordered.  Each 16-byte load of a wave then reads 1 KB in one piece,
+// where the token-major order made every load touch half of each of 16 key lines.
 struct LaneOffsets {
   int key, scale;
 };
@@ -48,7 +53,7 @@ template <int KFMT>
 __device__ __forceinline__ LaneOffsets lane_offsets(const PoolView& p, int g, int c) {
   LaneOffsets o;
   if (KFMT == DSA_IKEY_FP8) {
-    o.key = (int)p.ikey_off + c * DSA_INDEX_DIM + 16 * g;
+    o.key = (int)p.ikey_off + 16 * (16 * g + c);
     o.scale = (int)p.ikey_scale_off + (16 * g + c) * 4;
   } else {
     o.key = (int)p.ikey_off + c * (DSA_INDEX_DIM / 2) + 16 * g;
@@ -105,8 +110,8 @@ __device__ __forceinline__ void load_key_page(KeyFrag* f, float& scale, __amdgpu
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     if (KFMT == DSA_IKEY_FP8) {
-      const int k = o.key + nt * 16 * DSA_INDEX_DIM;
-      const uint4 lo = ld16<AUX>(rs, k), hi = ld16<AUX>(rs, k + 64);
+      const int k = o.key + nt * 2048;
+      const uint4 lo = ld16<AUX>(rs, k), hi = ld16<AUX>(rs, k + 1024);
       f[nt].b = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
                     (int)hi.w};
       f[nt].escale = 127;

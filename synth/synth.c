@@ -268,12 +268,22 @@ void synth_qmla(uint64_t seed, int64_t row0, int64_t nrows, uint16_t* q) {
 
 /* ---------------------------------------------------------------- pool writer */
 
+/* FP8 index keys of tokens [0, ntok) of a block into its key page, in the page's load order:
+ * byte b of slot t sits at 2048 (t / 16) + 1024 (b / 64) + 256 ((b / 16) % 4) + 16 (t % 16) + b % 16,
+ * so that the 16-byte pieces one 64-lane load takes (one per lane) form a contiguous 1 KB run. */
+static void put_fp8_keys(uint8_t* page, const uint8_t* key, int64_t ntok) {
+  for (int64_t t = 0; t < ntok; ++t)
+    for (int q = 0; q < IDX_DIM / 16; ++q)
+      memcpy(page + 2048 * (t / 16) + 1024 * (q / 4) + 256 * (q % 4) + 16 * (t % 16),
+             key + t * IDX_DIM + 16 * q, 16);
+}
+
 /*
  * Fill a block-packed pool.  Each pool row holds `block_size` tokens; the byte offsets inside a
  * row are given by the caller (they come from the library's layout descriptor):
  *   lat_off       latent page  [bs][576] e4m3   | NVFP4: [bs][288] packed e2m1
  *   lat_scale_off latent scale [bs] f32         | NVFP4: [bs][36] e4m3 block scales
- *   ikey_off      index keys   [bs][128] e4m3   | MXFP4: [bs][64] packed e2m1
+ *   ikey_off      index keys   [bs][128] e4m3 in load order (put_fp8_keys) | MXFP4: [bs][64] packed e2m1
  *   ikey_scale_off key scale   [bs] f32         | MXFP4: [bs][4] e8m0
  * Token s of sequence b lives in pool row block_table[b*ld_bt + s/bs], slot s%bs.  Slots past a
  * sequence's length and rows no sequence uses are filled with 0xFF bytes (NaN in E4M3, E8M0 and
@@ -335,7 +345,7 @@ void synth_fill_pool(uint64_t seed, int ikey_fmt, int lat_fmt, int block_size, i
           memcpy(row + lat_scale_off, lat_nv_scale, (size_t)(ntok * 36));
         }
         if (ikey_fmt == 0) {
-          memcpy(row + ikey_off, key, (size_t)(ntok * IDX_DIM));
+          put_fp8_keys(row + ikey_off, key, ntok);
           memcpy(row + ikey_scale_off, key_scale, (size_t)(ntok * 4));
         } else {
           memcpy(row + ikey_off, key, (size_t)(ntok * 64));
@@ -354,7 +364,7 @@ void synth_fill_pool(uint64_t seed, int ikey_fmt, int lat_fmt, int block_size, i
       }
       if (ikey_fmt == 0) {
         synth_ikey_fp8(seed, sid, tok0, ntok, key, key_scale);
-        memcpy(row + ikey_off, key, (size_t)(ntok * IDX_DIM));
+        put_fp8_keys(row + ikey_off, key, ntok);
         memcpy(row + ikey_scale_off, key_scale, (size_t)(ntok * 4));
       } else {
         synth_ikey_mxfp4(seed, sid, tok0, ntok, key, key_mx_scale);

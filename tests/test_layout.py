@@ -4,6 +4,7 @@ import numpy as np
 
 import sparse_attention_decode_amd as sad
 import synth
+from pool_layout import fp8_key_positions
 
 
 def _unpack_token(pool, kv, bt, s, wl):
@@ -17,7 +18,7 @@ def _unpack_token(pool, kv, bt, s, wl):
         lat = pool[base + kv.latent_off + slot * 288: base + kv.latent_off + slot * 288 + 288]
         ls = pool[base + kv.latent_scale_off + slot * 36: base + kv.latent_scale_off + slot * 36 + 36]
     if wl.ikey_fmt == 0:
-        key = pool[base + kv.ikey_off + slot * 128: base + kv.ikey_off + slot * 128 + 128]
+        key = pool[base + kv.ikey_off + fp8_key_positions(slot)]
         ks = pool[base + kv.ikey_scale_off + 4 * slot: base + kv.ikey_scale_off + 4 * slot + 4].view(np.float32)
     else:
         key = pool[base + kv.ikey_off + slot * 64: base + kv.ikey_off + slot * 64 + 64]

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import sparse_attention_decode_amd as sad
+from pool_layout import fp8_key_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +63,7 @@ def _expected_rows(kv, pool, slots, ikey, lat, write_keys=True, write_lat=True):
         j = s % bs
         if write_keys and kv.ikey_format == sad.IKEY_FP8:
             codes, sc = oracle.quant_fp8_token(ikey[t])
-            pool[base + kv.ikey_off + j * 128:][:128] = codes
+            pool[base + kv.ikey_off + fp8_key_positions(j)] = codes
             pool[base + kv.ikey_scale_off + 4 * j:][:4] = np.frombuffer(np.float32(sc).tobytes(),
                                                                          np.uint8)
         elif write_keys:
