@@ -107,7 +107,7 @@ struct MlaArgs {
   float tensor_scale;  // NVFP4 latent tensor scale (1 for FP8)
   uint16_t* out;       // [R][96][512] bf16
   float* lse;          // [R][96] or null
-  uint16_t* part_o;    // [R][split_slots][12 waves][16][64 lanes][4] fp16 normalised split outputs
+  uint16_t* part_o;    // [R][split_slots][12 waves][8][64 lanes][8] fp16 normalised split outputs
                        // * 2^part_exp, in the attention kernel's accumulator layout
   float* part_lse;     // [R][split_slots][96] base-2 log-sum-exp of each split
   int32_t* part_exp;   // [R][split_slots][96] power-of-two scale exponent of each split output

@@ -13,25 +13,29 @@
 //   out[r,h] = sum_j softmax(logit)_j * c_j[0:512]
 //
 // Design (gfx950).  A workgroup of 12 waves takes one row (or one split of its selected set).
-// Waves 2h and 2h+1 own heads [16h, 16h+16); wave 2h+d computes the half d of the QK contraction
-// (288 of the 576 dims) and the half d of the output dims (256 of 512), so a wave holds 36 query
-// registers and 64 accumulator registers, and three waves share each SIMD.  Tiles of 32 selected
-// tokens are gathered from the paged pool straight into LDS with direct global->LDS loads (no
-// registers held in flight), kStages - 1 tiles ahead of the tile being processed.  Each stage is
-// its own LDS variable and barriers wait on LDS traffic only, so reading a tile never waits for
-// the gathers of later tiles.  The pool rows to gather are handed over in a lane-distributed
+// Wave 4g + q belongs to head group g (heads [32g, 32g + 32)) and is its quarter q: it computes
+// the quarter q of the QK contraction (144 of the 576 dims) for the group's 32 heads and all 32
+// tokens of a tile, and the quarter q of the output dims (128 of 512), so it holds 36 query
+// registers and 64 accumulator registers, and three waves share each SIMD.  Both products use
+// the 32x32x16 MFMA shapes, which on this GPU issue at twice the rate per flop of the 16x16x32
+// ones, and every A operand read from LDS serves 32 heads.  Tiles of 32 selected tokens are
+// gathered from the paged pool straight into LDS with direct global->LDS loads (no registers
+// held in flight), kStages - 1 tiles ahead of the tile being processed.  Each stage is its own
+// LDS variable and barriers wait on LDS traffic only, so reading a tile never waits for the
+// gathers of later tiles.  The pool rows to gather are handed over in a lane-distributed
 // register (one batch of 21 tiles per register), read with readlane: no memory round trip sits
 // between a tile and its gathers.
 //   QK^T: S^T[tokens x heads] = C Q^T on bf16 MFMA.  The query stays in registers (B operand);
 //         the latent tile is the A operand.  FP8 latents are read raw from LDS and converted to
 //         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
-//         The two partial S^T of a wave pair are added through LDS (both waves then hold the
-//         same bits, so their softmax statistics agree exactly).
+//         The four quarter partials of S^T are exchanged through LDS so that quarter q ends up
+//         with the whole sum for tokens [8q, 8q + 8) (added in quarter order).
+//   softmax: quarter q turns its 8 tokens' logits into probabilities relative to its own
+//         largest logit and leaves them (fp16, times the token scale), that maximum and their
+//         sum in LDS; every wave of the group then reads all four, takes the tile maximum, and
+//         rescales each quarter's probabilities to the row's running maximum as it loads them.
 //   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  V^T comes from a dim-major fp16 copy of the
-//         value dims, converted once per tile for all head groups; P^T is S^T's softmax, already
-//         in B-operand position: the K order of this contraction is permuted so that lane group g
-//         holds tokens {4g..4g+3, 16+4g..16+4g+3}, and the dim-major tile stores tokens in that
-//         order.
+//         value dims, converted once per tile for all head groups.
 // Per-token scales stay out of the MFMA operands (they multiply the logits and the
 // probabilities), so every operand is an exact conversion of the stored codes.  fp16 for P keeps
 // its rounding well inside the output tolerance.  Softmax is online, in base 2.  With S^T and
@@ -45,11 +49,14 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWavesM = 2 * DSA_MLA_HEADS / 16;  // 12: 6 head groups x 2 halves
-constexpr int kThreadsM = kWavesM * kWave;        // 768
-constexpr int kTile = 32;                         // selected tokens per tile
-constexpr int kSteps = DSA_MLA_DQK / 32 / 2;      // 9 K steps of 32 dims per wave (half of 576)
-constexpr int kDvHalf = DSA_MLA_DV / 2;           // 256 output dims per wave
+constexpr int kHeadGroups = DSA_MLA_HEADS / 32;   // 3 groups of 32 heads
+constexpr int kQuarters = 4;                       // waves per head group
+constexpr int kWavesM = kHeadGroups * kQuarters;   // 12
+constexpr int kThreadsM = kWavesM * kWave;         // 768
+constexpr int kTile = 32;                          // selected tokens per tile
+constexpr int kQkSteps = DSA_MLA_DQK / kQuarters / 16;  // 9 K steps of 16 dims per wave
+constexpr int kDvTiles = DSA_MLA_DV / kQuarters / 32;   // 4 tiles of 32 output dims per wave
+constexpr int kPsRow = 80;                         // fp16 probability row: 32 tokens + pad
 #ifndef DSA_MLA_STAGES
 #define DSA_MLA_STAGES 3
 #endif
@@ -73,7 +80,7 @@ constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabil
 constexpr int kRaw8 = 592;   // raw row bytes: 576 codes + pad (148 dwords: b128 reads conflict-free)
 // NVFP4 latents
 constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
-constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords)
+constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords; rows 16-byte aligned)
 constexpr int kVt4 = 80;     // fp16 dim-major row bytes (both formats): 64 + pad (20 dwords)
 
 template <int LFMT>
@@ -121,13 +128,6 @@ __device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t voff, ui
 __device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" DSA_GATHER_POLICY
                :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
-}
-
-// Position of tile token t (quad q = t / 4, u = t % 4) in a dim-major row: the K slot that holds
-// it in the PV contraction.
-__device__ __forceinline__ int vt_pos(int t) {
-  const int q = t >> 2, u = t & 3;
-  return 8 * (q & 3) + 4 * (q >> 2) + u;
 }
 
 // Issue the direct global->LDS gathers of tile j (selected slots [j, min(j+32, jend))) into stage
@@ -188,8 +188,8 @@ __device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid)
       lo[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, false));
       hi[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, true));
     }
-    // dim row 4db+i: tokens 0..3 of the quad, K slots vt_pos(4 tq) .. +3
-    uint8_t* row = vt + 4 * db * kVt4 + 2 * vt_pos(4 * tq);
+    // dim row 4db+i: tokens 4 tq .. 4 tq + 3
+    uint8_t* row = vt + 4 * db * kVt4 + 8 * tq;
     *reinterpret_cast<uint2*>(row) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u),
                                            __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
     *reinterpret_cast<uint2*>(row + kVt4) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
@@ -224,16 +224,17 @@ __device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_
     crow[0] = uint4{w[0], w[1], w[2], w[3]};
     crow[1] = uint4{w[4], w[5], w[6], w[7]};
     if (16 * blk < DSA_MLA_DV) {
-      const int pos = vt_pos(t);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        *reinterpret_cast<uint16_t*>(vt + (16 * blk + i) * kVt4 + 2 * pos) = (uint16_t)f16_bits(v[i]);
+        *reinterpret_cast<uint16_t*>(vt + (16 * blk + i) * kVt4 + 2 * t) = (uint16_t)f16_bits(v[i]);
     }
   }
 }
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -244,11 +245,11 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(v8bf, r);
 }
 
-// K step i of contraction half dh: lane group g holds dims [288dh + 32i + 8g, +8).  The nine steps
-// of a half cover its 288 dims once; A and B operands use the same dims.
-constexpr int kHalfDims = DSA_MLA_DQK / 2;
+// QK K step i of quarter qt: lane (n, hi) holds dims [144 qt + 16 i + 8 hi, +8) of token n (A operand)
+// and of head n (B operand).  The nine steps of a quarter cover its 144 dims once.
+constexpr int kQuarterDims = DSA_MLA_DQK / kQuarters;  // 144
 
-// Latent tile as the A operand of QK^T: token t, dims [d, d+8) (d = 288dh + 32i + 8g).
+// Latent tile as the A operand of QK^T: token t, dims [d, d+8).
 template <int LFMT>
 __device__ __forceinline__ v8bf qk_operand(const Stage& st, const uint8_t* ct, int t, int d) {
   if constexpr (LFMT == DSA_LATENT_FP8) {
@@ -259,9 +260,19 @@ __device__ __forceinline__ v8bf qk_operand(const Stage& st, const uint8_t* ct, i
   }
 }
 
-// Dim-major fp16 value tile as the A operand of PV: dim row d, lane group g (8 K slots).
-__device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int g) {
-  return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 16 * g));
+// Dim-major fp16 value tile as the A operand of PV: dim row d, tokens [t0, t0 + 8).
+__device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int t0) {
+  return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 2 * t0));
+}
+
+// 32x32x16 MFMAs (bf16 for QK, fp16 for PV).  A lane l: row l % 32, K [8 (l / 32), +8); B lane l:
+// column l % 32, the same K; result register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
+// column l % 32.
+__device__ __forceinline__ v16f mfma32_bf16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma32_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // PHYS: the select's physical pool rows are given (else selected indices + block table).
@@ -273,24 +284,30 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t raw3[kStages > 3 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw4[kStages > 4 ? kRawBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t raw5[kStages > 5 ? kRawBytes : 16];
-  __shared__ __attribute__((aligned(16))) float tsc0[kSlots], tsc1[kSlots], tsc2[kSlots],
-      tsc3[kSlots], tsc4[kSlots], tsc5[kSlots];
+  constexpr int kTsc = G::kFp8 ? kSlots : 4;  // FP8 token scales (NVFP4 has none)
+  __shared__ __attribute__((aligned(16))) float tsc0[kTsc], tsc1[kTsc], tsc2[kTsc],
+      tsc3[kTsc], tsc4[kTsc], tsc5[kTsc];
   __shared__ __attribute__((aligned(16))) int32_t valid0[kTile], valid1[kTile], valid2[kTile],
       valid3[kTile], valid4[kTile],
       valid5[kTile];
   __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
-  __shared__ __attribute__((aligned(16))) v4f sx[kWavesM][2][kWave];  // partial S^T exchange
-  __shared__ float amx[kWavesM][16];
+  // partial S^T exchange: [head group][token quarter][source quarter, own one skipped][lane]
+  __shared__ __attribute__((aligned(16))) v4f sx[kHeadGroups][kQuarters][kQuarters - 1][kWave];
+  // probabilities (fp16) of a tile: [head group][head][token], rows padded to 80 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t ps[kHeadGroups * 32 * kPsRow];
+  // per head: each quarter's largest logit and its probability sum (relative to that logit)
+  __shared__ __attribute__((aligned(16))) float mqs[kHeadGroups][32][kQuarters];
+  __shared__ __attribute__((aligned(16))) float lqs[kHeadGroups][32][kQuarters];
   const Stage stages[6] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2},
                            {raw3, tsc3, valid3}, {raw4, tsc4, valid4}, {raw5, tsc5, valid5}};
 
   const int row = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave math scalar
-  const int g = lane >> 4, c = lane & 15;
-  const int dh = wave & 1;                // half of the QK dims and of the output dims
-  const int head = 16 * (wave >> 1) + c;  // this lane's head in S^T / O^T columns
+  const int n = lane & 31, hi = lane >> 5;
+  const int hg = wave >> 2, qt = wave & 3;  // head group (32 heads), quarter
+  const int head = 32 * hg + n;             // this lane's head in S^T / O^T columns
 
   const int32_t* idx = a.idx + (int64_t)row * a.k;
   const int32_t* prow = a.phys + (int64_t)row * a.k;
@@ -349,14 +366,14 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 
   // Prologue: the query loads go first (unconditional), the pool rows of the first batches right
   // behind them, so both round trips overlap.
-  // Q^T fragments (B operand) of this wave's half of the contraction
-  const int kd = kHalfDims * dh;  // first dim of the half (wave-uniform)
-  v8bf qf[kSteps];
+  // Q^T fragments (B operand) of this wave's quarter of the contraction
+  const int kd = kQuarterDims * qt;  // first dim of the quarter (wave-uniform)
+  v8bf qf[kQkSteps];
   {
-    const uint16_t* qr = a.q + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DQK + kd + 8 * g;
+    const uint16_t* qr = a.q + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DQK + kd + 8 * hi;
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i)
-      qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 32 * i));
+    for (int i = 0; i < kQkSteps; ++i)
+      qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 16 * i));
   }
   asm volatile("" ::: "memory");  // keep the query loads ahead of the pool-row loads
   int tb = 0;
@@ -366,15 +383,18 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   // the gathers are invisible to the compiler, and a wait of its own behind them would be a full
   // drain of the pipeline).
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) asm volatile("" ::"v"(qf[i]), "v"(pv), "v"(pv_next));
+  for (int i = 0; i < kQkSteps; ++i) asm volatile("" ::"v"(qf[i]), "v"(pv), "v"(pv_next));
 #pragma unroll
   for (int T = 0; T < kAhead; ++T)
     if (T < ntiles)
       issue_tile<LFMT>(stages[T], pv, kRowsPerWave * T, ph_spread, a, j0 + T * kTile, j1, lane);
 
-  v4f o[kDvHalf / 16];
+  // O^T (dims x heads) of this wave: dims [128 qt + 32 dt, +32) x the group's 32 heads
+  v16f o[kDvTiles];
 #pragma unroll
-  for (int mt = 0; mt < kDvHalf / 16; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < kDvTiles; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = a.softmax_scale * kLog2e;
 
@@ -397,93 +417,120 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       }
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
       const int tl = opaque((int)threadIdx.x);
-      const int ln = tl & 63, gl = ln >> 4, cl = ln & 15;
+      const int ln = tl & 63, nl = ln & 31, hl = ln >> 5;
       if constexpr (G::kFp8)
         build_fp8(cur, vt, tl);
       else
         build_nvfp4(cur, ct, vt, tl);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
-      // this wave's half of S^T (tokens x heads) for the two 16-token halves of the tile
-      v4f sfr[2];
+      // this wave's quarter of S^T (32 tokens x the group's 32 heads)
+      v16f acc;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < kSteps; ++i)
-          acc = mfma_bf16(qk_operand<LFMT>(cur, ct, 16 * h2 + cl, kd + 32 * i + 8 * gl), qf[i], acc);
-        sfr[h2] = acc;
-        sx[wave][h2][ln] = acc;
-      }
-      lds_barrier();  // partial S^T of both halves, and the value tile, are in LDS
+      for (int i = 0; i < kQkSteps; ++i)
+        acc = mfma32_bf16(qk_operand<LFMT>(cur, ct, nl, kd + 16 * i + 8 * hl), qf[i], acc);
+      // hand the token quarters of the other waves of the group their part of this partial
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) sfr[h2] += sx[wave ^ 1][h2][ln];
+      for (int rho = 0; rho < kQuarters; ++rho)
+        if (rho != qt)
+          sx[hg][rho][qt < rho ? qt : qt - 1][ln] =
+              v4f{acc[4 * rho], acc[4 * rho + 1], acc[4 * rho + 2], acc[4 * rho + 3]};
+      lds_barrier();  // partial S^T of every quarter, and the value tile, are in LDS
 
-      // logits in base 2; lane holds tokens 16*h2 + 4g + i for its head.  The four tokens'
-      // flags and scales are read at once, unconditionally; stale LDS bits of slots without a
-      // token are selected away, never used.
-      float x[2][4], ts[2][4];
-      float tmax = -INFINITY;
+      // S^T of this wave's token quarter: tokens 8 qt + 4 hl + i, head nl; the four partials
+      // are added in quarter order
+      v4f sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int t0 = 16 * h2 + 4 * gl;
-        const int4 ok4 = *reinterpret_cast<const int4*>(cur.valid + t0);
-        const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
-        float scv[4] = {a.tensor_scale, a.tensor_scale, a.tensor_scale, a.tensor_scale};
-        if constexpr (G::kFp8) {
-          const float4 s4 = *reinterpret_cast<const float4*>(cur.tsc + t0);
-          scv[0] = s4.x; scv[1] = s4.y; scv[2] = s4.z; scv[3] = s4.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = okv[i] != 0;
-          const float scl = ok ? scv[i] : 0.f;
-          ts[h2][i] = scl;
-          const float v = ok ? sfr[h2][i] * scl * qk_scale : -INFINITY;
-          x[h2][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+      for (int src = 0; src < kQuarters; ++src) {
+        const v4f p = (src == qt) ? v4f{acc[4 * qt], acc[4 * qt + 1], acc[4 * qt + 2], acc[4 * qt + 3]}
+                                  : sx[hg][qt][src < qt ? src : src - 1][ln];
+        sq = (src == 0) ? p : sq + p;
       }
-      tmax = xor32_max(xor16_max(tmax));
+
+      // logits in base 2; the four tokens' flags and scales are read at once, unconditionally;
+      // stale LDS bits of slots without a token are selected away, never used
+      const int t0 = 8 * qt + 4 * hl;
+      const int4 ok4 = *reinterpret_cast<const int4*>(cur.valid + t0);
+      const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
+      float scv[4] = {a.tensor_scale, a.tensor_scale, a.tensor_scale, a.tensor_scale};
+      if constexpr (G::kFp8) {
+        const float4 s4 = *reinterpret_cast<const float4*>(cur.tsc + t0);
+        scv[0] = s4.x; scv[1] = s4.y; scv[2] = s4.z; scv[3] = s4.w;
+      }
+      float x[4], ts[4];
+      float mq = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = okv[i] != 0;
+        ts[i] = ok ? scv[i] : 0.f;
+        x[i] = ok ? sq[i] * ts[i] * qk_scale : -INFINITY;
+        mq = fmaxf(mq, x[i]);
+      }
+      mq = xor32_max(mq);  // the quarter's 8 tokens
+      // probabilities relative to the quarter's own largest logit (<= 1); the reader rescales
+      // them to the row's running maximum.  A quarter without tokens has p = 0.
+      const float mrq = (mq == -INFINITY) ? 0.f : mq;
+      float psq = 0.f;
+      uint32_t pw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * i] - mrq);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * i + 1] - mrq);
+        psq += p0 + p1;
+        // the token scale of c_j multiplies its value row
+        pw[i] = f16_bits(p0 * ts[2 * i]) | (f16_bits(p1 * ts[2 * i + 1]) << 16);
+      }
+      psq = xor32_sum(psq);
+      *reinterpret_cast<uint2*>(ps + (32 * hg + nl) * kPsRow + 2 * t0) = uint2{pw[0], pw[1]};
+      if (hl == 0) {
+        mqs[hg][nl][qt] = mq;
+        lqs[hg][nl][qt] = psq;
+      }
+      lds_barrier();  // every quarter's probabilities, maxima and sums are in LDS
+
       // Lazy rescaling: the running max only moves when a logit exceeds it by more than 2^4, so
       // probabilities stay <= 16 and O is rarely rescaled.  The fp16 probability times the token
-      // scale must stay finite: token (or tensor) scales below 4096.
+      // scale must stay finite: token (or tensor) scales below 4096.  Every wave of the group
+      // computes the same values from the same LDS words.
+      const float4 m4 = *reinterpret_cast<const float4*>(&mqs[hg][nl][0]);
+      const float4 l4 = *reinterpret_cast<const float4*>(&lqs[hg][nl][0]);
+      const float mqv[4] = {m4.x, m4.y, m4.z, m4.w};
+      const float lqv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float tmax = fmaxf(fmaxf(mqv[0], mqv[1]), fmaxf(mqv[2], mqv[3]));
       const float m_old = m_run;
       const float m_new = (tmax > m_run + kLazyMax) ? tmax : m_run;
       // v_exp_f32 directly (exp2(-inf) = 0; results below the fp32 normal range flush to zero,
       // negligible next to the token that set the running max, whose probability is 1)
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float mref = (m_new == -INFINITY) ? 0.f : m_new;  // all logits -inf: p = 0, not NaN
-      float psum = 0.f;
-      uint32_t pb[4];
+      float fq[4], psum = 0.f;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(x[h2][i] - mref);
-          psum += p;
-          pv[i] = p * ts[h2][i];  // the token scale of c_j multiplies its value row
-        }
-        // K slots 8g + 4*h2 + i  <->  token 16*h2 + 4g + i
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          pb[2 * h2 + i] = f16_bits(pv[2 * i]) | (f16_bits(pv[2 * i + 1]) << 16);
+      for (int q = 0; q < 4; ++q) {
+        fq[q] = (mqv[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mqv[q] - mref);
+        psum += lqv[q] * fq[q];
       }
-      psum = xor32_sum(xor16_sum(psum));
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      const v8h pfrag = __builtin_bit_cast(v8h, uint4{pb[0], pb[1], pb[2], pb[3]});
       // wave-uniform, rarely taken; never while the running max is still -inf (O is all zeros)
       if (__builtin_amdgcn_readfirstlane(__any(alpha != 1.f && m_old != -INFINITY))) {
 #pragma unroll
-        for (int mt = 0; mt < kDvHalf / 16; ++mt) o[mt] *= alpha;
+        for (int dt = 0; dt < kDvTiles; ++dt) o[dt] *= alpha;
       }
 
-      // O^T (dims x heads) += V^T P^T; A operand lane: dim 256dh + 16mt + c, K slots 8g .. 8g+7
+      // O^T (dims x heads) += V^T P^T, 16 tokens per step: tokens [16 ks + 8 hl, +8) of head nl
+      // come from quarter 2 ks + hl, rescaled to the running maximum
 #pragma unroll
-      for (int mt = 0; mt < kDvHalf / 16; ++mt)
-        o[mt] = mfma_f16(pv_operand(vt, kDvHalf * dh + 16 * mt + cl, gl), pfrag, o[mt]);
+      for (int ks = 0; ks < 2; ++ks) {
+        v8h pf = __builtin_bit_cast(
+            v8h, *reinterpret_cast<const uint4*>(ps + (32 * hg + nl) * kPsRow + 2 * (16 * ks + 8 * hl)));
+        const _Float16 f = (_Float16)(hl ? fq[2 * ks + 1] : fq[2 * ks]);
+        pf *= f;
+#pragma unroll
+        for (int dt = 0; dt < kDvTiles; ++dt)
+          o[dt] = mfma32_f16(pv_operand(vt, 128 * qt + 32 * dt + nl, 16 * ks + 8 * hl), pf, o[dt]);
+      }
 
       // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
       // first barrier, so no one reads it any more).  Issued last: a wave that finds the gather
@@ -505,59 +552,71 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   // the gathers issued ahead of the last tiles (dummies) land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // lane holds O^T[256dh + 16mt + 4g + i][head]
+  // lane holds O^T[128 qt + 32 dt + 8 b + 4 hi + i][head] in o[dt][4 b + i]
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   if (a.out_direct) {
-    uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + kDvHalf * dh;
+    uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + 128 * qt + 4 * hi;
 #pragma unroll
-    for (int mt = 0; mt < kDvHalf / 16; ++mt) {
-      uint32_t b[4];
+    for (int dt = 0; dt < kDvTiles; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t u = __float_as_uint(o[mt][i] * inv);
-        b[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      for (int b = 0; b < 4; ++b) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t u = __float_as_uint(o[dt][4 * b + i] * inv);
+          w[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        }
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * b) = uint2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
       }
-      *reinterpret_cast<uint2*>(orow + 16 * mt + 4 * g) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-    }
-    if (a.lse && g == 0 && dh == 0)
+    if (a.lse && qt == 0 && hi == 0)
       a.lse[(int64_t)row * DSA_MLA_HEADS + head] =
           (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     // Split partial: this split's normalised output as fp16 scaled by a power of two chosen from
     // the head's largest value in the split (11 significant bits relative to that value, for any
     // latent scale), the scale's exponent, and the split's base-2 log-sum-exp.  The fp16 values
-    // keep the accumulator layout (wave, mt, lane, 4 values), so every store is 512 contiguous
-    // bytes.
+    // keep the accumulator layout (wave, register octet, lane, 8 values), so every store is
+    // 1,024 contiguous bytes.
     const int64_t slot = ((int64_t)row * a.split_slots + a.split_base + split) * DSA_MLA_HEADS + head;
     float amax = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < kDvHalf / 16; ++mt)
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o[mt][0]), fabsf(o[mt][1])),
-                               fmaxf(fabsf(o[mt][2]), fabsf(o[mt][3]))));
+    for (int dt = 0; dt < kDvTiles; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[dt][r]));
     amax *= inv;
-    amax = xor32_max(xor16_max(amax));
-    if (g == 0) amx[wave][c] = amax;
+    amax = xor32_max(amax);
+    // the partial S^T exchange area is free once every wave has passed the last tile's third
+    // barrier, which it has before any wave gets here
+    float (*amx)[32][kQuarters] = reinterpret_cast<float (*)[32][kQuarters]>(&sx[0][0][0][0]);
+    if (hi == 0) amx[hg][n][qt] = amax;
     lds_barrier();
-    amax = fmaxf(amax, amx[wave ^ 1][c]);  // over all 512 dims of the head
+    {
+      const float4 m4 = *reinterpret_cast<const float4*>(&amx[hg][n][0]);
+      amax = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));  // over all 512 dims of the head
+    }
     // 2^e * amax lies in [2^14, 2^15): well inside fp16's range and above its subnormals
     const int e = (amax > 0.f) ? 14 - ilogbf(amax) : 0;
     const float sc = inv * ldexpf(1.f, e);
-    uint2* po = reinterpret_cast<uint2*>(a.part_o) +
-                (((int64_t)row * a.split_slots + a.split_base + split) * kWavesM + wave) *
-                    (kDvHalf / 16) * kWave + lane;
+    uint4* po = reinterpret_cast<uint4*>(a.part_o) +
+                (((int64_t)row * a.split_slots + a.split_base + split) * kWavesM + wave) * 8 * kWave +
+                lane;
 #pragma unroll
-    for (int mt = 0; mt < kDvHalf / 16; ++mt) {
+    for (int oc = 0; oc < 8; ++oc) {
       // Large partial sets are streamed out (non-temporal): read once by the combine, they
       // should not sit dirty in the memory-side cache and be written back while the next step's
       // scorer streams keys.  Small ones stay cached for the combine.
-      const v2u w = {f16_bits(o[mt][0] * sc) | (f16_bits(o[mt][1] * sc) << 16),
-                     f16_bits(o[mt][2] * sc) | (f16_bits(o[mt][3] * sc) << 16)};
+      const v16f& od = o[oc >> 1];
+      const int r0 = 8 * (oc & 1);
+      const v4u w = {f16_bits(od[r0] * sc) | (f16_bits(od[r0 + 1] * sc) << 16),
+                     f16_bits(od[r0 + 2] * sc) | (f16_bits(od[r0 + 3] * sc) << 16),
+                     f16_bits(od[r0 + 4] * sc) | (f16_bits(od[r0 + 5] * sc) << 16),
+                     f16_bits(od[r0 + 6] * sc) | (f16_bits(od[r0 + 7] * sc) << 16)};
       if (a.nt_partials)
-        __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(po + mt * kWave));
+        __builtin_nontemporal_store(w, reinterpret_cast<v4u*>(po + oc * kWave));
       else
-        *reinterpret_cast<v2u*>(po + mt * kWave) = w;
+        *reinterpret_cast<v4u*>(po + oc * kWave) = w;
     }
-    if (g == 0 && dh == 0) {
+    if (qt == 0 && hi == 0) {
       a.part_lse[slot] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
       a.part_exp[slot] = e;
     }
@@ -565,33 +624,32 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 }
 
 // Merge the splits of each row by log-sum-exp: out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
-// with o_s the split's normalised output.  grid (rows, 12 waves x 2 halves); 512 threads: thread
-// (mt8, lane) takes accumulator block mt = 8 * blockIdx.y % 2 + mt8 of the attention wave
-// blockIdx.y / 2, i.e. head 16 * (wave / 2) + lane % 16, dims 256 * (wave % 2) + 16 mt + 4 (lane / 16)
-// + 0..3.  Partial loads are 8 contiguous bytes per thread (4 KB per workgroup and split).
+// with o_s the split's normalised output.  grid (rows, 12 attention waves); 512 threads: thread
+// (oc, lane) takes register octet oc of the attention wave blockIdx.y, i.e. head
+// 32 (wave / 4) + lane % 32 and dims 128 (wave % 4) + 32 (oc / 2) + 16 (oc % 2) + 4 (lane / 32)
+// + {0..3, 8..11}.  Partial loads are 16 contiguous bytes per thread (8 KB per workgroup and split).
 // G: splits per group (4, 8 or 16), the smallest that covers nsplit when it can.
 template <int G>
 __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   const int row = blockIdx.x;
-  const int wave = blockIdx.y >> 1;
-  const int mt = 8 * (blockIdx.y & 1) + (threadIdx.x >> 6);
+  const int wave = blockIdx.y;
+  const int oc = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int head = 16 * (wave >> 1) + (lane & 15);
-  const int d = kDvHalf * (wave & 1) + 16 * mt + 4 * (lane >> 4);
+  const int head = 32 * (wave >> 2) + (lane & 31);
+  const int d = 128 * (wave & 3) + 32 * (oc >> 1) + 16 * (oc & 1) + 4 * (lane >> 5);
   const int64_t hbase = (int64_t)row * a.split_slots * DSA_MLA_HEADS + head;
-  const uint2* pbase = reinterpret_cast<const uint2*>(a.part_o) +
-                       ((int64_t)row * a.split_slots * kWavesM + wave) * (kDvHalf / 16) * kWave +
-                       mt * kWave + lane;
-  const int64_t pstride = (int64_t)kWavesM * (kDvHalf / 16) * kWave;  // one split
+  const uint4* pbase = reinterpret_cast<const uint4*>(a.part_o) +
+                       ((int64_t)row * a.split_slots * kWavesM + wave) * 8 * kWave + oc * kWave + lane;
+  const int64_t pstride = (int64_t)kWavesM * 8 * kWave;  // one split
   // One pass over groups of G splits: every load of a group (log-sum-exp, exponent and partial)
   // is in flight before any is used, and a running maximum rescales what earlier groups added,
   // so up to G splits take one memory round trip.
   float M = -INFINITY, L = 0.f;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.split_slots; s0 += G) {
     float ls[G];
     int ex[G];
-    uint2 v[G];
+    uint4 v[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int sp = min(s0 + u, a.split_slots - 1);  // past the end: a repeat, weighted 0 below
@@ -608,29 +666,32 @@ __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
     const float r = exp2f(M - m_new);  // M = -inf: 0 (L and acc are 0 then)
     L *= r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= r;
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
     M = m_new;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const float wgt = (s0 + u < a.split_slots && ls[u] != -INFINITY) ? exp2f(ls[u] - M) : 0.f;
       L += wgt;
       const float w2 = ldexpf(wgt, -ex[u]);
-      acc[0] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x & 0xFFFFu));
-      acc[1] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].x >> 16));
-      acc[2] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y & 0xFFFFu));
-      acc[3] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u].y >> 16));
+      const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(vw[i] & 0xFFFFu));
+        acc[2 * i + 1] += w2 * (float)__builtin_bit_cast(_Float16, (uint16_t)(vw[i] >> 16));
+      }
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  uint32_t b[4];
+  uint32_t b[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     uint32_t u = __float_as_uint(acc[i] * inv);
     b[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   }
-  *reinterpret_cast<uint2*>(a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + d) =
-      uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-  if (a.lse && mt == 0 && (wave & 1) == 0 && lane < 16)
+  uint16_t* orow = a.out + ((int64_t)row * DSA_MLA_HEADS + head) * DSA_MLA_DV + d;
+  *reinterpret_cast<uint2*>(orow) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+  *reinterpret_cast<uint2*>(orow + 8) = uint2{b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+  if (a.lse && oc == 0 && (wave & 3) == 0 && lane < 32)
     a.lse[(int64_t)row * DSA_MLA_HEADS + head] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -680,7 +741,7 @@ size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant) {
 
 hipError_t launch_mla_combine(const MlaArgs& a, hipStream_t s) {
   if (a.batch.num_rows <= 0) return hipSuccess;
-  const dim3 cgrid((unsigned)a.batch.num_rows, 2 * kWavesM);
+  const dim3 cgrid((unsigned)a.batch.num_rows, kWavesM);
   if (a.split_slots <= 4)
     hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
   else if (a.split_slots <= 8)
