@@ -189,6 +189,73 @@ def time_front(wl, d, kv, steps: int):
             "achieved_GBps": nbytes / (us * 1e-6) / 1e9}
 
 
+def time_front_overlap(wl, layers, devs, kvs, reps: int, steps: int):
+    """The step before the path together with the layer, by the host clock over `steps` steps:
+    the layer alone; the front then the layer on one stream; and the front with its latent write
+    (dsa_cache_append, latents only) on a second stream beside the scorer and the select, the
+    attention waiting for it (an event).  Both streams keep the default priority.  The side stream
+    also waits for the previous step's attention before it rewrites the new tokens' latents."""
+    import torch
+    import sparse_attention_decode_amd as sad
+    R = wl.num_rows
+    pos = wl.row_pos.astype(np.int64)
+    slots = wl.block_table[wl.row_seq, pos // wl.block_size].astype(np.int64) * wl.block_size \
+        + pos % wl.block_size
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + 29)
+    bf = lambda *shape: torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    d_slot = torch.from_numpy(slots).cuda()
+    ikey, lat, q = bf(R, 128), bf(R, 576), bf(R, 32, 128)
+    w = torch.randn(R, 32, generator=g, device="cuda")
+    q_idx = torch.empty(R, 32, 128, dtype=torch.uint8, device="cuda")
+    w_out = torch.empty_like(w)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev_start = [torch.cuda.Event() for _ in range(4)]
+    ev_lat = [torch.cuda.Event() for _ in range(4)]
+
+    def layer_only(i):
+        j = i % reps
+        layers[j].scores_step(devs[j]["pool"], devs[j]["q_idx"], devs[j]["w"])
+        layers[j].topk_step()
+        layers[j].attention_step(devs[j]["pool"], devs[j]["q"])
+
+    def serial(i):
+        j = i % reps
+        sad.dsa_indexer_front(kvs[j], devs[j]["pool"], d_slot, ikey, q, w, q_idx, w_out)
+        sad.dsa_cache_append(kvs[j], devs[j]["pool"], d_slot, latent=lat)
+        layer_only(i)
+
+    def overlapped(i):
+        j = i % reps
+        e0, e1 = ev_start[i % 4], ev_lat[i % 4]
+        e0.record(main)
+        side.wait_event(e0)
+        with torch.cuda.stream(side):
+            sad.dsa_cache_append(kvs[j], devs[j]["pool"], d_slot, latent=lat, stream=side)
+        e1.record(side)
+        sad.dsa_indexer_front(kvs[j], devs[j]["pool"], d_slot, ikey, q, w, q_idx, w_out)
+        layers[j].scores_step(devs[j]["pool"], devs[j]["q_idx"], devs[j]["w"])
+        layers[j].topk_step()
+        main.wait_event(e1)
+        layers[j].attention_step(devs[j]["pool"], devs[j]["q"])
+
+    out = {}
+    for name, fn in (("layer_ms_per_step", layer_only), ("serial_ms_per_step", serial),
+                     ("overlapped_ms_per_step", overlapped)):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        out[name] = 1e3 * (time.perf_counter() - t0) / steps
+    out["front_serial_us"] = 1e3 * (out["serial_ms_per_step"] - out["layer_ms_per_step"])
+    out["front_overlapped_us"] = 1e3 * (out["overlapped_ms_per_step"] - out["layer_ms_per_step"])
+    out["steps"] = steps
+    return out
+
+
 def read_ceiling(wls, devs, kvs, reps: int = 10):
     """Measured read ceilings after the timed region (dsa_probe_read: loads only, no
     arithmetic): (a) exactly the scorer's key pages, block by block in the block tables' order,
@@ -350,6 +417,8 @@ def main():
                          "for the workload as measured (candidates for the 8,192-row prefill "
                          "chunk, dense elsewhere)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip timing the step before the path together with the layer")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--dcp", type=int, default=0,
                     help="emulate decode context parallelism: the workload split into this many "
@@ -509,6 +578,9 @@ def main():
     }
     # the step before the path, timed on its own after the layer (not part of `value`)
     result["front"] = time_front(wl, devs[0], kvs[0], max(10, min(args.steps, 100)))
+    if not use_graph and not args.no_overlap:
+        result["front"]["with_layer"] = time_front_overlap(wl, layers, devs, kvs, reps,
+                                                           max(10, min(args.steps, 50)))
     if not args.no_cpu:
         log("[bench] timing the oracle on a CPU sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_budget)
