@@ -69,9 +69,11 @@ constexpr int kSlots = kRowsPerWave * kWavesM;                  // 36 LDS rows p
 // Pool rows of a wave's gathers, one register per batch of tiles: lane 3T + r holds the row of
 // tile T's row r of the batch (kBatchTiles tiles per register).
 constexpr int kBatchTiles = kWave / kRowsPerWave;  // 21
-// Every wave issues exactly this many gathers per tile (data + scale per row, dummies included),
-// so waiting for a tile is "all but the newest tile's gathers are done".
-constexpr int kGathersPerWave = 2 * kRowsPerWave;
+// Every wave issues exactly this many gathers per tile (FP8: one per row, its scale included;
+// NVFP4: data + block scales per row; dummies included), so waiting for a tile is "all but the
+// newest tile's gathers are done".
+template <int LFMT>
+constexpr int kGathersPerWave = (LFMT == DSA_LATENT_FP8 ? 1 : 2) * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabilities <= 16)
@@ -156,10 +158,14 @@ __device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int 
     const int slot = src & (kBlock - 1);
     uint8_t* dst = st.raw + t * G::kRaw;
     if constexpr (G::kFp8) {
+      // lanes 0..35 copy the 576 latent bytes, lane 36 the 16 bytes from the token's scale on
+      // (its fp32 scale, then the next slots' scales or the index-key page: still inside the
+      // pool row) into the row's 16-byte pad: one gather instruction per row
       const uint8_t* lat = row + a.pool.lat_off + slot * DSA_MLA_DQK;
-      const uint8_t* scl = row + a.pool.lat_scale_off + slot * 4;
-      if (lane < DSA_MLA_DQK / 16) lds_copy16(lat, 16 * lane, lds_addr(dst));
-      if (lane == 0) lds_copy4(scl, 0, lds_addr(st.tsc + t));
+      const uint32_t scl_off = (uint32_t)(a.pool.lat_scale_off - a.pool.lat_off) +
+                               (uint32_t)slot * (4u - DSA_MLA_DQK);  // > 0: scales follow latents
+      if (lane <= DSA_MLA_DQK / 16)
+        lds_copy16(lat, lane < DSA_MLA_DQK / 16 ? 16u * lane : scl_off, lds_addr(dst));
     } else {
       const uint8_t* lat = row + a.pool.lat_off + slot * (DSA_MLA_DQK / 2);
       const uint8_t* scl = row + a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16);
@@ -175,6 +181,8 @@ __device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int 
 // into four dim rows of 4 tokens.  Tokens that are not selected get zeros, so their (zero)
 // probabilities never meet stale data.
 __device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid) {
+  // the tokens' scales, gathered into each row's pad, side by side for the softmax
+  if (tid < kTile) st.tsc[tid] = *reinterpret_cast<const float*>(st.raw + tid * kRaw8 + DSA_MLA_DQK);
   for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
     const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
     // the four tokens' flags in one read; every row read unconditionally, then selected
@@ -409,10 +417,11 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       {
         const int newer = min(kAhead - 1, ntiles - 1 - (j - j0) / kTile);
         static_assert(kAhead - 1 <= 4, "wait counts below");
-        if (newer >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kGathersPerWave) : "memory");
-        else if (newer == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kGathersPerWave) : "memory");
-        else if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kGathersPerWave) : "memory");
-        else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGathersPerWave) : "memory");
+        constexpr int kG = kGathersPerWave<LFMT>;
+        if (newer >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kG) : "memory");
+        else if (newer == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kG) : "memory");
+        else if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kG) : "memory");
+        else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
@@ -494,6 +503,13 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // probabilities stay <= 16 and O is rarely rescaled.  The fp16 probability times the token
       // scale must stay finite: token (or tensor) scales below 4096.  Every wave of the group
       // computes the same values from the same LDS words.
+      // the probabilities of this lane's PV operands are read with the maxima and sums, so that
+      // the three reads take one LDS round trip
+      v8h pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pf[ks] = __builtin_bit_cast(
+            v8h, *reinterpret_cast<const uint4*>(ps + (32 * hg + nl) * kPsRow + 2 * (16 * ks + 8 * hl)));
       const float4 m4 = *reinterpret_cast<const float4*>(&mqs[hg][nl][0]);
       const float4 l4 = *reinterpret_cast<const float4*>(&lqs[hg][nl][0]);
       const float mqv[4] = {m4.x, m4.y, m4.z, m4.w};
@@ -523,13 +539,11 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // come from quarter 2 ks + hl, rescaled to the running maximum
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        v8h pf = __builtin_bit_cast(
-            v8h, *reinterpret_cast<const uint4*>(ps + (32 * hg + nl) * kPsRow + 2 * (16 * ks + 8 * hl)));
         const _Float16 f = (_Float16)(hl ? fq[2 * ks + 1] : fq[2 * ks]);
-        pf *= f;
+        const v8h p = pf[ks] * f;
 #pragma unroll
         for (int dt = 0; dt < kDvTiles; ++dt)
-          o[dt] = mfma32_f16(pv_operand(vt, 128 * qt + 32 * dt + nl, 16 * ks + 8 * hl), pf, o[dt]);
+          o[dt] = mfma32_f16(pv_operand(vt, 128 * qt + 32 * dt + nl, 16 * ks + 8 * hl), p, o[dt]);
       }
 
       // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
