@@ -132,45 +132,47 @@ __device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uin
                :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
 }
 
-// Issue the direct global->LDS gathers of tile j (selected slots [j, min(j+32, jend))) into stage
-// st.  Wave w gathers tile rows w, w+12, w+24, whose pool rows are lanes lb, lb+1, lb+2 of `pv`.
-// Rows past the tile (slots 32..35 of the stage) and slots without a token gather a dummy row,
-// so that every wave issues kGathersPerWave loads per tile: the wave's first real row of the
-// tile again if it has one, else `ph_spread`, a pool row that depends on the workgroup and wave
-// (never one row for everybody: thousands of requests to one address would queue on one memory
-// channel).  Every gather lands in the stage's own LDS variable, and its pool row is
-// wave-uniform (scalar base address, 32-bit lane offset).
+// Gather sources of one wave for a batch of kBatchTiles tiles, one register set per batch: lane
+// 3T + r holds, for row wave + 12 r of tile T of the batch, the byte offset from the pool base of
+// what that row gathers (its latent, or a dummy row's: see below), bit 63 set when the row holds
+// a selected, visible token, and (NVFP4) the offset of the row's block scales from its latent.
+// Everything that depends on the selection is resolved here, once per batch, so issuing a tile's
+// gathers is a few scalar instructions per row.
+struct GatherSrc {
+  uint32_t lo, hi;   // byte offset (bits 0..62) and the valid flag (bit 63)
+  uint32_t scl;      // NVFP4: block scales - latent, in bytes (positive: the scale page follows)
+};
+
+// Issue the direct global->LDS gathers of tile T of the current batch into stage st: wave w
+// gathers tile rows w, w+12, w+24 (lanes 3T, 3T+1, 3T+2 of `src`).  Rows past the tile (slots
+// 32..35 of the stage) and slots without a token gather a dummy row, so that every wave issues
+// kGathersPerWave loads per tile.  Every gather lands in the stage's own LDS variable, and its
+// source is wave-uniform (scalar base address, 32-bit lane offset).
 template <int LFMT>
-__device__ __forceinline__ void issue_tile(const Stage& st, int pv, int lb, int ph_spread,
-                                           const MlaArgs& a, int j, int jend, int lane) {
+__device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src, int T,
+                                           const MlaArgs& a, int lane) {
   using G = Geo<LFMT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ph_first = (j + wave < jend) ? __builtin_amdgcn_readlane(pv, lb) : -1;
-  const int ph_dummy = ph_first >= 0 ? ph_first : ph_spread;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int t = wave + kWavesM * r;  // < kSlots
-    const int jj = j + t;
-    const int ph = (t < kTile && jj < jend) ? __builtin_amdgcn_readlane(pv, lb + r) : -1;
-    if (t < kTile && lane == 0) st.valid[t] = ph >= 0;
-    const int src = __builtin_amdgcn_readfirstlane(ph >= 0 ? ph : ph_dummy);  // >= 0
-    const uint8_t* row = a.pool.base + (int64_t)(src >> 6) * a.pool.row_bytes;
-    const int slot = src & (kBlock - 1);
+    const int l = kRowsPerWave * T + r;
+    const uint32_t lo = __builtin_amdgcn_readlane(src.lo, l);
+    const uint32_t hi = __builtin_amdgcn_readlane(src.hi, l);
+    if (t < kTile && lane == 0) st.valid[t] = (int)(hi >> 31);
+    const uint8_t* row = a.pool.base + ((((uint64_t)(hi & 0x7FFFFFFFu)) << 32) | lo);
     uint8_t* dst = st.raw + t * G::kRaw;
     if constexpr (G::kFp8) {
       // lanes 0..35 copy the 576 latent bytes, lane 36 the 16 bytes from the token's scale on
       // (its fp32 scale, then the next slots' scales or the index-key page: still inside the
       // pool row) into the row's 16-byte pad: one gather instruction per row
-      const uint8_t* lat = row + a.pool.lat_off + slot * DSA_MLA_DQK;
-      const uint32_t scl_off = (uint32_t)(a.pool.lat_scale_off - a.pool.lat_off) +
-                               (uint32_t)slot * (4u - DSA_MLA_DQK);  // > 0: scales follow latents
+      const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
       if (lane <= DSA_MLA_DQK / 16)
-        lds_copy16(lat, lane < DSA_MLA_DQK / 16 ? 16u * lane : scl_off, lds_addr(dst));
+        lds_copy16(row, lane < DSA_MLA_DQK / 16 ? 16u * lane : scl, lds_addr(dst));
     } else {
-      const uint8_t* lat = row + a.pool.lat_off + slot * (DSA_MLA_DQK / 2);
-      const uint8_t* scl = row + a.pool.lat_scale_off + slot * (DSA_MLA_DQK / 16);
-      if (lane < DSA_MLA_DQK / 32) lds_copy16(lat, 16 * lane, lds_addr(dst));
-      if (lane < DSA_MLA_DQK / 64) lds_copy4(scl, 4 * lane, lds_addr(dst + DSA_MLA_DQK / 2));
+      const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
+      if (lane < DSA_MLA_DQK / 32) lds_copy16(row, 16u * lane, lds_addr(dst));
+      if (lane < DSA_MLA_DQK / 64) lds_copy4(row, scl + 4u * lane, lds_addr(dst + DSA_MLA_DQK / 2));
     }
   }
 }
@@ -343,7 +345,9 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   // Pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane 3T + r:
   // tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  // dummy gather row of this wave when a tile has no real row for it (see issue_tile)
+  // A row without a token gathers a dummy row: the wave's first real row of the tile again if
+  // it has one, else a pool row that depends on the workgroup and wave (never one row for
+  // everybody: thousands of requests to one address would queue on one memory channel).
   const int ph_spread = __builtin_amdgcn_readfirstlane(
       (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens));
   auto load_batch = [&](int tb) {
@@ -369,7 +373,19 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         if (!ok && a.status) atomicOr(a.status, DSA_DEVERR_BLOCK_ID);
       }
     }
-    return ph;
+    const int first = __shfl(ph, kRowsPerWave * T);  // row 0 of this wave in the same tile
+    const int src = ph >= 0 ? ph : (first >= 0 ? first : ph_spread);
+    const int slot = src & (kBlock - 1);
+    constexpr int kLat = G::kFp8 ? DSA_MLA_DQK : DSA_MLA_DQK / 2;  // latent bytes per token
+    constexpr int kScl = G::kFp8 ? 4 : DSA_MLA_DQK / 16;            // scale bytes per token
+    const uint64_t off = (uint64_t)(src >> 6) * (uint64_t)a.pool.row_bytes +
+                         (uint64_t)a.pool.lat_off + (uint64_t)(slot * kLat);
+    GatherSrc g;
+    g.lo = (uint32_t)off;
+    g.hi = (uint32_t)(off >> 32) | (ph >= 0 ? 0x80000000u : 0u);
+    g.scl = (uint32_t)(a.pool.lat_scale_off - a.pool.lat_off) + (uint32_t)slot * kScl -
+            (uint32_t)slot * kLat;
+    return g;
   };
 
   // Prologue: the query loads go first (unconditional), the pool rows of the first batches right
@@ -385,17 +401,18 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   }
   asm volatile("" ::: "memory");  // keep the query loads ahead of the pool-row loads
   int tb = 0;
-  int pv = load_batch(0);
-  int pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : -1;
+  GatherSrc pv = load_batch(0);
+  GatherSrc pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : pv;
   // The pool rows and the query arrive together (one wait, before the first gather is issued:
   // the gathers are invisible to the compiler, and a wait of its own behind them would be a full
   // drain of the pipeline).
 #pragma unroll
-  for (int i = 0; i < kQkSteps; ++i) asm volatile("" ::"v"(qf[i]), "v"(pv), "v"(pv_next));
+  for (int i = 0; i < kQkSteps; ++i)
+    asm volatile("" ::"v"(qf[i]), "v"(pv.lo), "v"(pv.hi), "v"(pv.scl), "v"(pv_next.lo),
+                 "v"(pv_next.hi), "v"(pv_next.scl));
 #pragma unroll
   for (int T = 0; T < kAhead; ++T)
-    if (T < ntiles)
-      issue_tile<LFMT>(stages[T], pv, kRowsPerWave * T, ph_spread, a, j0 + T * kTile, j1, lane);
+    if (T < ntiles) issue_tile<LFMT>(stages[T], pv, T, a, lane);
 
   // O^T (dims x heads) of this wave: dims [128 qt + 32 dt, +32) x the group's 32 heads
   v16f o[kDvTiles];
@@ -556,9 +573,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
           pv = pv_next;
           if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
         }
-        if (T < ntiles)
-          issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, kRowsPerWave * (T - tb), ph_spread, a,
-                           j + kAhead * kTile, j1, ln);
+        if (T < ntiles) issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, T - tb, a, ln);
       }
     }
   }
