@@ -217,7 +217,10 @@ void indexer_kernel(IndexerArgs a) {
   // their head weights (rows past nr repeat the last row; their results are never used).
   const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   const int my_blk = blk0 + wave + kWaves * lane;
-  const int bt_raw = bt[min((int64_t)map_block(my_blk), a.batch.ld_bt - 1)];
+  // lane i: the sequence block of this wave's page i (the candidate pass's mapping divides by
+  // S - 1; done once per lane here, the page loop reads it back with readlane)
+  const int my_map = map_block(my_blk);
+  const int bt_raw = bt[min((int64_t)my_map, a.batch.ld_bt - 1)];
   uint4 qv[kQPer];
   float wl[kWPer];
 #pragma unroll
@@ -328,7 +331,7 @@ void indexer_kernel(IndexerArgs a) {
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const float cur_scale = bscale[u & 1];
-      const int blk = map_block(page_of(i));
+      const int blk = MODE == kScoreDense ? page_of(i) : __builtin_amdgcn_readlane(my_map, i & 63);
       // The rows' queries and weights come from LDS one row ahead of their use, so each row's
       // reads are in flight while the previous row is scored.  Not hoisted further: out of the
       // page loop they would hold 24 registers per row for the whole kernel.
@@ -424,7 +427,8 @@ void indexer_kernel(IndexerArgs a) {
       const int i = i0 + u;
       if (i >= ppw || page_of(i) >= nblk) break;
       const int lp = page_of(i);
-      const int s_tok = map_block(lp) * kBlock + lane;  // the token (visibility)
+      const int s_tok = (MODE == kScoreDense ? lp : __builtin_amdgcn_readlane(my_map, i & 63)) * kBlock +
+                        lane;  // the token (visibility)
       const int s_at = lp * kBlock + lane;               // its place in this launch's scores
 #pragma unroll
       for (int r = 0; r < R; ++r) {
