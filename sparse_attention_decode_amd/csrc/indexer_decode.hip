@@ -352,7 +352,10 @@ void indexer_kernel(IndexerArgs a) {
       float wv[2][4];
       load_row(0, qa, wv);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {  // all R rows (rows past nr score with the last row's query)
+      for (int r = 0; r < R; ++r) {
+        // a tile with fewer rows than R (a shorter sequence in a mixed batch, the last tile of
+        // a prefill chunk) skips the rest: nr is wave-uniform
+        if (r >= nr) break;
         asm volatile("" ::: "memory");  // at most two rows' queries live
         if (!kPrefetchRow && r > 0) load_row(r, qa, wv);
         v8i qn[2];
@@ -404,6 +407,7 @@ void indexer_kernel(IndexerArgs a) {
         const int tok = blk * kBlock + lane;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+          if (r >= nr) break;
           const uint32_t key = order_key(sbuf[r][u]);
           const bool keep = r < nr && tok <= pos[r] &&
                             (key > fT[r] || (key == fT[r] && tok < fI[r]));
