@@ -218,7 +218,7 @@ void indexer_kernel(IndexerArgs a) {
   const int32_t* bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   const int my_blk = blk0 + wave + kWaves * lane;
   // lane i: the sequence block of this wave's page i (the candidate pass's mapping divides by
-  // S - 1; done once per lane here, the page loop reads it back with readlane)
+  // S - 1: done once per lane here, and its page loop reads it back with readlane)
   const int my_map = map_block(my_blk);
   const int bt_raw = bt[min((int64_t)my_map, a.batch.ld_bt - 1)];
   uint4 qv[kQPer];
@@ -331,7 +331,7 @@ void indexer_kernel(IndexerArgs a) {
       if (i >= ppw || page_of(i) >= nblk) break;
       const KeyFrag* cur = buf[u & 1];
       const float cur_scale = bscale[u & 1];
-      const int blk = MODE == kScoreDense ? page_of(i) : __builtin_amdgcn_readlane(my_map, i & 63);
+      const int blk = MODE == kScoreCand ? __builtin_amdgcn_readlane(my_map, i & 63) : map_block(page_of(i));
       // The rows' queries and weights come from LDS one row ahead of their use, so each row's
       // reads are in flight while the previous row is scored.  Not hoisted further: out of the
       // page loop they would hold 24 registers per row for the whole kernel.
@@ -353,9 +353,11 @@ void indexer_kernel(IndexerArgs a) {
       load_row(0, qa, wv);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        // a tile with fewer rows than R (a shorter sequence in a mixed batch, the last tile of
-        // a prefill chunk) skips the rest: nr is wave-uniform
-        if (r >= nr) break;
+        // a dense decode tile with fewer rows than R (a shorter sequence in a mixed batch) skips
+        // the rest (nr is wave-uniform).  Not in the 16-row prefill tile, whose rows are all
+        // present but in a chunk's last tile (the branch cost its pipelined row loop 7%), nor in
+        // the candidate pass (measured slower with it).
+        if (MODE == kScoreDense && !kPrefetchRow && r >= nr) break;
         asm volatile("" ::: "memory");  // at most two rows' queries live
         if (!kPrefetchRow && r > 0) load_row(r, qa, wv);
         v8i qn[2];
@@ -407,7 +409,6 @@ void indexer_kernel(IndexerArgs a) {
         const int tok = blk * kBlock + lane;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if (r >= nr) break;
           const uint32_t key = order_key(sbuf[r][u]);
           const bool keep = r < nr && tok <= pos[r] &&
                             (key > fT[r] || (key == fT[r] && tok < fI[r]));
@@ -431,8 +432,7 @@ void indexer_kernel(IndexerArgs a) {
       const int i = i0 + u;
       if (i >= ppw || page_of(i) >= nblk) break;
       const int lp = page_of(i);
-      const int s_tok = (MODE == kScoreDense ? lp : __builtin_amdgcn_readlane(my_map, i & 63)) * kBlock +
-                        lane;  // the token (visibility)
+      const int s_tok = map_block(lp) * kBlock + lane;  // the token (visibility)
       const int s_at = lp * kBlock + lane;               // its place in this launch's scores
 #pragma unroll
       for (int r = 0; r < R; ++r) {
