@@ -22,9 +22,11 @@
 // gathered from the paged pool straight into LDS with direct global->LDS loads (no registers
 // held in flight), kStages - 1 tiles ahead of the tile being processed.  Each stage is its own
 // LDS variable and barriers wait on LDS traffic only, so reading a tile never waits for the
-// gathers of later tiles.  The pool rows to gather are handed over in a lane-distributed
-// register (one batch of 21 tiles per register), read with readlane: no memory round trip sits
-// between a tile and its gathers.
+// gathers of later tiles.  FP8: the split's pool rows are resolved once into an LDS list, and a
+// tile is gathered as 16-byte chunks at consecutive LDS addresses, two full 64-lane gathers per
+// wave with a 64-bit address per lane (no per-row scalar work, no exec masking).  NVFP4: the pool
+// rows to gather are handed over in a lane-distributed register (one batch of 21 tiles per
+// register) and read with readlane, one latent and one scale gather per row.
 //   QK^T: S^T[tokens x heads] = C Q^T on bf16 MFMA.  The query stays in registers (B operand);
 //         the latent tile is the A operand.  FP8 latents are read raw from LDS and converted to
 //         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
@@ -69,17 +71,28 @@ constexpr int kSlots = kRowsPerWave * kWavesM;                  // 36 LDS rows p
 // Pool rows of a wave's gathers, one register per batch of tiles: lane 3T + r holds the row of
 // tile T's row r of the batch (kBatchTiles tiles per register).
 constexpr int kBatchTiles = kWave / kRowsPerWave;  // 21
-// Every wave issues exactly this many gathers per tile (FP8: one per row, its scale included;
-// NVFP4: data + block scales per row; dummies included), so waiting for a tile is "all but the
-// newest tile's gathers are done".
+// Every gathering wave issues exactly this many gathers per tile (FP8: two chunk gathers; NVFP4:
+// data + block scales per row, dummies included), so waiting for a tile is "all but the newest
+// tiles' gathers are done".
 template <int LFMT>
-constexpr int kGathersPerWave = (LFMT == DSA_LATENT_FP8 ? 1 : 2) * kRowsPerWave;
+constexpr int kGathersPerWave = LFMT == DSA_LATENT_FP8 ? 2 : 2 * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabilities <= 16)
 
 // FP8 latents
 constexpr int kRaw8 = 592;   // raw row bytes: 576 codes + pad (148 dwords: b128 reads conflict-free)
+// FP8 tiles are copied as 16-byte chunks: chunk c of a tile is part c % 37 of row c / 37 (parts
+// 0..35: the 576 latent bytes; part 36: the 16 bytes from the token's scale on, into the row's
+// pad), so the tile is 1,184 chunks at consecutive LDS addresses.  Waves 0..9 copy chunks
+// [128 w, 128 w + 128) in two full 64-lane gathers; the last 96 (past the 32 rows) land in the
+// stage's spare rows.  Waves 10 and 11 copy nothing.
+constexpr int kChunks8 = kRaw8 / 16;                // 37 per row
+constexpr int kTileChunks8 = kTile * kChunks8;      // 1184 per tile
+constexpr int kWaveChunks8 = 2 * kWave;             // 128 per gathering wave
+constexpr int kGatherWaves8 = (kTileChunks8 + kWaveChunks8 - 1) / kWaveChunks8;  // 10
+static_assert(kGatherWaves8 <= kWavesM, "FP8 gathers");
+static_assert(kGatherWaves8 * kWaveChunks8 * 16 <= kSlots * kRaw8, "FP8 gathers stay in the stage");
 // NVFP4 latents
 constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
 constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords; rows 16-byte aligned)
@@ -99,7 +112,7 @@ struct Geo {
 struct Stage {
   uint8_t* raw;    // [kSlots][kRaw] latent rows as stored (rows >= kTile: dummy gathers)
   float* tsc;      // [kSlots] FP8 token scales
-  int32_t* valid;  // [kTile] slot holds a selected, visible token
+  int32_t* valid;  // NVFP4: [kTile] >= 0 where the slot holds a selected, visible token, else -1
 };
 
 // The value of x, opaque to the optimiser: lane-dependent addresses derived from it inside the tile
@@ -132,6 +145,38 @@ __device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uin
                :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
 }
 
+// One chunk gather with a 64-bit address per lane: lane l copies 16 bytes from addr to LDS
+// address lds + 16 l.
+__device__ __forceinline__ void lds_copy16_va(uint64_t addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" DSA_GATHER_POLICY
+               :: "v"(addr), "s"(lds) : "memory", "m0");
+}
+
+// FP8: the chunk gathers of one tile into stage st.  rows: the tile's 32 pool rows (-1: no
+// token; such a row gathers pool row `spare` instead, whose data is never used).  Each lane finds
+// its chunk's row in LDS and forms the address itself, so the wave issues two instructions and
+// no per-row scalar work.  Chunks past the tile read row 31's last chunk again.
+__device__ __forceinline__ void issue_tile_fp8(const Stage& st, const int32_t* rows, const MlaArgs& a,
+                                               int wave, int lane, int spare) {
+  if (wave >= kGatherWaves8) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = min(kWaveChunks8 * wave + kWave * i + lane, kTileChunks8 - 1);
+    const int t = c / kChunks8, part = c - kChunks8 * t;
+    const int ph = rows[t];
+    const uint32_t src = (uint32_t)(ph >= 0 ? ph : spare);
+    const uint32_t slot = src & (kBlock - 1);
+    // offsets inside a pool row fit 32 bits; the latent or the scale offset picked by a mask,
+    // not a branch
+    const uint32_t lat = (uint32_t)a.pool.lat_off + slot * DSA_MLA_DQK + 16u * part;
+    const uint32_t scl = (uint32_t)a.pool.lat_scale_off + slot * 4u;
+    const uint32_t within = scl ^ ((lat ^ scl) & (0u - (uint32_t)(part < DSA_MLA_DQK / 16)));
+    const uint64_t addr = reinterpret_cast<uint64_t>(a.pool.base) +
+                          (uint64_t)(src >> 6) * (uint32_t)a.pool.row_bytes + within;
+    lds_copy16_va(addr, lds_addr(st.raw + 16 * (kWaveChunks8 * wave + kWave * i)));
+  }
+}
+
 // Gather sources of one wave for a batch of kBatchTiles tiles, one register set per batch: lane
 // 3T + r holds, for row wave + 12 r of tile T of the batch, the byte offset from the pool base of
 // what that row gathers (its latent, or a dummy row's: see below), bit 63 set when the row holds
@@ -159,7 +204,7 @@ __device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src
     const int l = kRowsPerWave * T + r;
     const uint32_t lo = __builtin_amdgcn_readlane(src.lo, l);
     const uint32_t hi = __builtin_amdgcn_readlane(src.hi, l);
-    if (t < kTile && lane == 0) st.valid[t] = (int)(hi >> 31);
+    if (t < kTile && lane == 0) st.valid[t] = (int)(hi >> 31) - 1;
     const uint8_t* row = a.pool.base + ((((uint64_t)(hi & 0x7FFFFFFFu)) << 32) | lo);
     uint8_t* dst = st.raw + t * G::kRaw;
     if constexpr (G::kFp8) {
@@ -182,19 +227,20 @@ __device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src
 // per token give its four values as two half-word pairs, and half-word permutes transpose them
 // into four dim rows of 4 tokens.  Tokens that are not selected get zeros, so their (zero)
 // probabilities never meet stale data.
-__device__ __forceinline__ void build_fp8(const Stage& st, uint8_t* vt, int tid) {
+__device__ __forceinline__ void build_fp8(const Stage& st, const int32_t* rows, uint8_t* vt, int tid) {
   // the tokens' scales, gathered into each row's pad, side by side for the softmax
   if (tid < kTile) st.tsc[tid] = *reinterpret_cast<const float*>(st.raw + tid * kRaw8 + DSA_MLA_DQK);
   for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
     const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
-    // the four tokens' flags in one read; every row read unconditionally, then selected
-    const int4 ok = *reinterpret_cast<const int4*>(st.valid + 4 * tq);
+    // the four tokens' pool rows in one read (>= 0: a token); every row read unconditionally,
+    // then selected
+    const int4 ok = *reinterpret_cast<const int4*>(rows + 4 * tq);
     const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
     uint32_t lo[4], hi[4];  // token u: fp16 of dims (4db, 4db+1) and of (4db+2, 4db+3)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t r = *reinterpret_cast<const uint32_t*>(st.raw + (4 * tq + u) * kRaw8 + 4 * db);
-      r = okv[u] ? r : 0u;
+      r = okv[u] >= 0 ? r : 0u;
       lo[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, false));
       hi[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, true));
     }
@@ -217,7 +263,7 @@ __device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_
   for (int it = tid; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
     const int t = it & 31, blk = it >> 5;  // token, 16-dim block
     float v[16];
-    if (st.valid[t]) {
+    if (st.valid[t] >= 0) {
       const uint2 p = *reinterpret_cast<const uint2*>(st.raw + t * kRaw4 + 8 * blk);
       const float s = fp8_to_f32(st.raw[t * kRaw4 + DSA_MLA_DQK / 2 + blk]);
       fp4x8_scaled_to_f32x8(p.x, s, v);
@@ -297,15 +343,18 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   constexpr int kTsc = G::kFp8 ? kSlots : 4;  // FP8 token scales (NVFP4 has none)
   __shared__ __attribute__((aligned(16))) float tsc0[kTsc], tsc1[kTsc], tsc2[kTsc],
       tsc3[kTsc], tsc4[kTsc], tsc5[kTsc];
-  __shared__ __attribute__((aligned(16))) int32_t valid0[kTile], valid1[kTile], valid2[kTile],
-      valid3[kTile], valid4[kTile],
-      valid5[kTile];
+  constexpr int kValid = G::kFp8 ? 4 : kTile;  // NVFP4 row flags (FP8 takes them from plist)
+  __shared__ __attribute__((aligned(16))) int32_t valid0[kValid], valid1[kValid], valid2[kValid],
+      valid3[kValid], valid4[kValid], valid5[kValid];
   __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
   // partial S^T exchange: [head group][token quarter][source quarter, own one skipped][lane]
   __shared__ __attribute__((aligned(16))) v4f sx[kHeadGroups][kQuarters][kQuarters - 1][kWave];
   // probabilities (fp16) of a tile: [head group][head][token], rows padded to 80 bytes
   __shared__ __attribute__((aligned(16))) uint8_t ps[kHeadGroups * 32 * kPsRow];
+  // FP8: pool rows of the split's selected entries in order (-1: no visible token), padded with
+  // -1 to whole tiles (a split never spans more than k <= DSA_MAX_TOPK entries)
+  __shared__ __attribute__((aligned(16))) int32_t plist[G::kFp8 ? DSA_MAX_TOPK : 4];
   // per head: each quarter's largest logit and its probability sum (relative to that logit)
   __shared__ __attribute__((aligned(16))) float mqs[kHeadGroups][32][kQuarters];
   __shared__ __attribute__((aligned(16))) float lqs[kHeadGroups][32][kQuarters];
@@ -350,6 +399,28 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   // everybody: thousands of requests to one address would queue on one memory channel).
   const int ph_spread = __builtin_amdgcn_readfirstlane(
       (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens));
+  // The pool row of the split's selected entry jj, or -1 where there is none (past the split's
+  // end, an empty or invisible entry, or a pool row or block outside the pool: the last two are
+  // also reported in the status word).
+  auto resolve = [&](int jj) {
+    int ph = -1;
+    if (jj < j1) {
+      if (PHYS) {
+        const int v = prow[jj];
+        ph = v < a.pool.tokens ? v : -1;
+        if (v >= a.pool.tokens && a.status) atomicOr(a.status, DSA_DEVERR_POOL_ROW);
+      } else {
+        const int sidx = idx[jj];
+        if (sidx >= 0 && sidx < nvis) {
+          const int b = bt[sidx / kBlock];
+          const bool ok = b >= 0 && (int64_t)b * kBlock < a.pool.tokens;
+          ph = ok ? b * kBlock + (sidx % kBlock) : -1;
+          if (!ok && a.status) atomicOr(a.status, DSA_DEVERR_BLOCK_ID);
+        }
+      }
+    }
+    return ph;
+  };
   auto load_batch = [&](int tb) {
     const int T = lane / kRowsPerWave, r = lane % kRowsPerWave;
     const int t = wave + kWavesM * r;
@@ -401,18 +472,41 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   }
   asm volatile("" ::: "memory");  // keep the query loads ahead of the pool-row loads
   int tb = 0;
-  GatherSrc pv = load_batch(0);
-  GatherSrc pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : pv;
-  // The pool rows and the query arrive together (one wait, before the first gather is issued:
-  // the gathers are invisible to the compiler, and a wait of its own behind them would be a full
-  // drain of the pipeline).
+  GatherSrc pv = {0u, 0u, 0u}, pv_next = {0u, 0u, 0u};
+  if constexpr (G::kFp8) {
+    // the split's pool rows, resolved once: every load in flight at once, then one LDS barrier
+    constexpr int kIters = (DSA_MAX_TOPK + kThreadsM - 1) / kThreadsM;
+    int ph[kIters];
 #pragma unroll
-  for (int i = 0; i < kQkSteps; ++i)
-    asm volatile("" ::"v"(qf[i]), "v"(pv.lo), "v"(pv.hi), "v"(pv.scl), "v"(pv_next.lo),
-                 "v"(pv_next.hi), "v"(pv_next.scl));
+    for (int it = 0; it < kIters; ++it) ph[it] = resolve(j0 + tid + kThreadsM * it);
 #pragma unroll
-  for (int T = 0; T < kAhead; ++T)
-    if (T < ntiles) issue_tile<LFMT>(stages[T], pv, T, a, lane);
+    for (int it = 0; it < kIters; ++it) {
+      const int e = tid + kThreadsM * it;
+      if (e < ntiles * kTile) plist[e] = ph[it];
+    }
+    lds_barrier();
+    // The query has arrived too (one wait, before the first gather is issued: the gathers are
+    // invisible to the compiler, and a wait of its own behind them would be a full drain of the
+    // pipeline).
+#pragma unroll
+    for (int i = 0; i < kQkSteps; ++i) asm volatile("" ::"v"(qf[i]));
+#pragma unroll
+    for (int T = 0; T < kAhead; ++T)
+      if (T < ntiles) issue_tile_fp8(stages[T], plist + kTile * T, a, wave, lane, ph_spread);
+  } else {
+    pv = load_batch(0);
+    pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : pv;
+    // The pool rows and the query arrive together (one wait, before the first gather is issued:
+    // the gathers are invisible to the compiler, and a wait of its own behind them would be a
+    // full drain of the pipeline).
+#pragma unroll
+    for (int i = 0; i < kQkSteps; ++i)
+      asm volatile("" ::"v"(qf[i]), "v"(pv.lo), "v"(pv.hi), "v"(pv.scl), "v"(pv_next.lo),
+                   "v"(pv_next.hi), "v"(pv_next.scl));
+#pragma unroll
+    for (int T = 0; T < kAhead; ++T)
+      if (T < ntiles) issue_tile<LFMT>(stages[T], pv, T, a, lane);
+  }
 
   // O^T (dims x heads) of this wave: dims [128 qt + 32 dt, +32) x the group's 32 heads
   v16f o[kDvTiles];
@@ -444,8 +538,9 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
       const int tl = opaque((int)threadIdx.x);
       const int ln = tl & 63, nl = ln & 31, hl = ln >> 5;
+      const int32_t* rows = G::kFp8 ? plist + (j - j0) : cur.valid;  // >= 0: a token
       if constexpr (G::kFp8)
-        build_fp8(cur, vt, tl);
+        build_fp8(cur, rows, vt, tl);
       else
         build_nvfp4(cur, ct, vt, tl);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
@@ -478,7 +573,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // logits in base 2; the four tokens' flags and scales are read at once, unconditionally;
       // stale LDS bits of slots without a token are selected away, never used
       const int t0 = 8 * qt + 4 * hl;
-      const int4 ok4 = *reinterpret_cast<const int4*>(cur.valid + t0);
+      const int4 ok4 = *reinterpret_cast<const int4*>(rows + t0);
       const int okv[4] = {ok4.x, ok4.y, ok4.z, ok4.w};
       float scv[4] = {a.tensor_scale, a.tensor_scale, a.tensor_scale, a.tensor_scale};
       if constexpr (G::kFp8) {
@@ -489,7 +584,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       float mq = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = okv[i] != 0;
+        const bool ok = okv[i] >= 0;
         ts[i] = ok ? scv[i] : 0.f;
         x[i] = ok ? sq[i] * ts[i] * qk_scale : -INFINITY;
         mq = fmaxf(mq, x[i]);
@@ -568,12 +663,17 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // queue full stalls here, where it would otherwise wait at the next barrier.
       {
         const int T = (j - j0) / kTile + kAhead;
-        if (T - tb == kBatchTiles) {  // next batch of pool rows (loaded one batch ahead)
-          tb += kBatchTiles;
-          pv = pv_next;
-          if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
+        if constexpr (G::kFp8) {
+          if (T < ntiles)
+            issue_tile_fp8(stages[(s + kAhead) % kStages], plist + kTile * T, a, wave, ln, ph_spread);
+        } else {
+          if (T - tb == kBatchTiles) {  // next batch of pool rows (loaded one batch ahead)
+            tb += kBatchTiles;
+            pv = pv_next;
+            if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
+          }
+          if (T < ntiles) issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, T - tb, a, ln);
         }
-        if (T < ntiles) issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, T - tb, a, ln);
       }
     }
   }
