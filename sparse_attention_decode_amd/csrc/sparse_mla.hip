@@ -391,12 +391,11 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     bt = a.batch.block_table + (int64_t)seq * a.batch.ld_bt;
   }
 
-  // Pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane 3T + r:
-  // tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  // A row without a token gathers a dummy row: the wave's first real row of the tile again if
-  // it has one, else a pool row that depends on the workgroup and wave (never one row for
-  // everybody: thousands of requests to one address would queue on one memory channel).
+  // A row without a token gathers a spare row whose data is never used: a pool row that depends
+  // on the workgroup and wave (never one row for everybody: thousands of requests to one address
+  // would queue on one memory channel); NVFP4 takes the wave's first real row of the tile instead
+  // when it has one.
   const int ph_spread = __builtin_amdgcn_readfirstlane(
       (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens));
   // The pool row of the split's selected entry jj, or -1 where there is none (past the split's
@@ -421,6 +420,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     }
     return ph;
   };
+  // NVFP4: pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane
+  // 3T + r: tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
   auto load_batch = [&](int tb) {
     const int T = lane / kRowsPerWave, r = lane % kRowsPerWave;
     const int t = wave + kWavesM * r;
@@ -459,8 +460,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     return g;
   };
 
-  // Prologue: the query loads go first (unconditional), the pool rows of the first batches right
-  // behind them, so both round trips overlap.
+  // Prologue: the query loads go first (unconditional), the pool rows (FP8: the split's whole
+  // list; NVFP4: the first batches) right behind them, so both round trips overlap.
   // Q^T fragments (B operand) of this wave's quarter of the contraction
   const int kd = kQuarterDims * qt;  // first dim of the quarter (wave-uniform)
   v8bf qf[kQkSteps];
