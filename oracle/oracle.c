@@ -11,8 +11,9 @@
  *         "Sparse Attention in K3.1 Pro", "KV cache footprint", "A KV cache for three kinds of
  *         state", "AMD / Quantization: Native MXFP4 indexer".
  *   [K31] also, section "Low-latency decode: a fused DSA decode path", for the step before the
- *         path: the indexer query quantised with its head weights folded in, and the new token's
- *         index key and latent written into the cache (the quantisers at the end of this file).
+ *         path: the indexer query quantised after the head weights are multiplied into it, and the
+ *         new token's index key and latent written into the cache (the quantisers at the end of
+ *         this file).
  *   The pages defer the indexer's scoring rule to DeepSeek-V3.2's lightning indexer; the rule
  *   used here is that indexer's: score = sum_h w[h] * ReLU(scale_s * q[h] . k[s]).
  *   Number formats follow their published definitions: OCP 8-bit Floating Point (E4M3),
