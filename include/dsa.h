@@ -195,8 +195,8 @@ DSA_API dsa_status dsa_topk(const dsa_kv_layout* kv, const dsa_batch* batch, con
                             size_t workspace_bytes, void* stream);
 
 /*
- * Steps 1 and 2 without stored scores: the candidates path (page: a scorer and an exact top-k
- * select in two kernels, §Low-latency decode: a fused DSA decode path).  The scores of a full row
+ * Steps 1 and 2 without stored scores: the candidates path (page: two kernels, a scorer and then an
+ * exact top-k select, §Low-latency decode: a fused DSA decode path).  The scores of a full row
  * are never written; the select receives only the tokens that can still make the row's top-k.
  *   dsa_indexer_candidates  scores a sample of each sequence (every S-th 64-token block, S a power
  *       of two near sqrt(max_context / 2k), chosen by the library), takes the sample's exact
@@ -278,7 +278,7 @@ DSA_API dsa_status sparse_mla_decode_noalloc(const dsa_kv_layout* kv, const void
 /*
  * The step before the path ("vLLM Delivers Day-0 Support for Kimi K3.1 Pro", §Low-latency decode:
  * a fused DSA decode path: the indexer query is quantised with the head weights merged into its
- * scale, and the new token's index key and latent go into the KV cache, the latent write
+ * scale, and the appended token's index key and latent go into the KV cache, the latent write
  * overlapping the indexer).  Rounding is to the nearest code, ties to the even code, saturating at the format's
  * largest finite value; inputs must be finite.  The codes are exact functions of the bf16 inputs.
  *

@@ -12,7 +12,7 @@
  *         state", "AMD / Quantization: Native MXFP4 indexer".
  *   [K31] also, section "Low-latency decode: a fused DSA decode path", for the step before the
  *         path: the indexer query quantised after the head weights are multiplied into it, and the
- *         new token's index key and latent written into the cache (the quantisers at the end of
+ *         appended token's index key and latent written into the cache (the quantisers at the end of
  *         this file).
  *   The pages defer the indexer's scoring rule to DeepSeek-V3.2's lightning indexer; the rule
  *   used here is that indexer's: score = sum_h w[h] * ReLU(scale_s * q[h] . k[s]).
@@ -301,7 +301,7 @@ int64_t orc_dsa_rows(int key_fmt, int lat_fmt, int nrows, const int64_t* row_pos
 }
 
 /* ------------------------------------------------------------------ quantisers (the step
- * before the path: the new token's index key and latent written into its paged row, and the
+ * before the path: the appended token's index key and latent written into its paged row, and the
  * indexer query quantised with its scale folded into the head weight; [K31] "A KV cache for three
  * kinds of state" for the formats, "Low-latency decode: a fused DSA decode path" for the step).
  *

@@ -2,8 +2,8 @@
 // scores are never stored in full.
 //
 // Source: "vLLM Delivers Day-0 Support for Kimi K3.1 Pro" — §Low-latency decode: a fused DSA
-// decode path (a scorer and an exact top-k select in two kernels, the select emitting physical KV
-// rows); §Sparse Attention in K3.1 Pro (keep the 2,048 highest-scoring tokens); §AMD /
+// decode path (two kernels: a scorer, then an exact top-k select whose output is the pool rows
+// to gather); §Sparse Attention in K3.1 Pro (keep the 2,048 highest-scoring tokens); §AMD /
 // Communication (a consistent tie rule: here the lower token index wins, -0 ties +0).
 //
 // Why a candidate list is exact.  The scorer first scores a sample of each sequence (every S-th
