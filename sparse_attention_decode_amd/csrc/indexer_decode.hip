@@ -515,9 +515,11 @@ hipError_t launch_cand_rows(const IndexerArgs& a, int rows, dim3 grid, hipStream
                            dim3(kThreads), 0, s, a);
       break;
     case kPrefillRows:
-      if (MODE != kScoreSample) return hipErrorInvalidValue;  // the candidate pass takes 8 rows
-      hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false, false, kThreads, MODE>),
-                         grid, dim3(kThreads), 0, s, a);
+      if constexpr (MODE == kScoreSample)
+        hipLaunchKernelGGL((indexer_kernel<kPrefillRows, KFMT, false, false, kThreads, MODE>),
+                           grid, dim3(kThreads), 0, s, a);
+      else
+        return hipErrorInvalidValue;  // the candidate pass takes 8-row tiles
       break;
     default:
       return hipErrorInvalidValue;
