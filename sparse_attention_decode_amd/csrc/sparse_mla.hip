@@ -177,10 +177,11 @@ __device__ __forceinline__ void issue_tile_fp8(const Stage& st, const int32_t* r
   }
 }
 
-// Gather sources of one wave for a batch of kBatchTiles tiles, one register set per batch: lane
-// 3T + r holds, for row wave + 12 r of tile T of the batch, the byte offset from the pool base of
-// what that row gathers (its latent, or a dummy row's: see below), bit 63 set when the row holds
-// a selected, visible token, and (NVFP4) the offset of the row's block scales from its latent.
+// NVFP4: gather sources of one wave for a batch of kBatchTiles tiles, one register set per
+// batch: lane 3T + r holds, for row wave + 12 r of tile T of the batch, the byte offset from the
+// pool base of what that row gathers (its latent, or a dummy row's: see below), bit 63 set when
+// the row holds a selected, visible token, and the offset of the row's block scales from its
+// latent.
 // Everything that depends on the selection is resolved here, once per batch, so issuing a tile's
 // gathers is a few scalar instructions per row.
 struct GatherSrc {
@@ -188,8 +189,8 @@ struct GatherSrc {
   uint32_t scl;      // NVFP4: block scales - latent, in bytes (positive: the scale page follows)
 };
 
-// Issue the direct global->LDS gathers of tile T of the current batch into stage st: wave w
-// gathers tile rows w, w+12, w+24 (lanes 3T, 3T+1, 3T+2 of `src`).  Rows past the tile (slots
+// NVFP4: issue the direct global->LDS gathers of tile T of the current batch into stage st: wave
+// w gathers tile rows w, w+12, w+24 (lanes 3T, 3T+1, 3T+2 of `src`).  Rows past the tile (slots
 // 32..35 of the stage) and slots without a token gather a dummy row, so that every wave issues
 // kGathersPerWave loads per tile.  Every gather lands in the stage's own LDS variable, and its
 // source is wave-uniform (scalar base address, 32-bit lane offset).
@@ -197,6 +198,7 @@ template <int LFMT>
 __device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src, int T,
                                            const MlaArgs& a, int lane) {
   using G = Geo<LFMT>;
+  static_assert(!G::kFp8, "FP8 tiles are gathered as chunks (issue_tile_fp8)");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
@@ -207,18 +209,9 @@ __device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src
     if (t < kTile && lane == 0) st.valid[t] = (int)(hi >> 31) - 1;
     const uint8_t* row = a.pool.base + ((((uint64_t)(hi & 0x7FFFFFFFu)) << 32) | lo);
     uint8_t* dst = st.raw + t * G::kRaw;
-    if constexpr (G::kFp8) {
-      // lanes 0..35 copy the 576 latent bytes, lane 36 the 16 bytes from the token's scale on
-      // (its fp32 scale, then the next slots' scales or the index-key page: still inside the
-      // pool row) into the row's 16-byte pad: one gather instruction per row
-      const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
-      if (lane <= DSA_MLA_DQK / 16)
-        lds_copy16(row, lane < DSA_MLA_DQK / 16 ? 16u * lane : scl, lds_addr(dst));
-    } else {
-      const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
-      if (lane < DSA_MLA_DQK / 32) lds_copy16(row, 16u * lane, lds_addr(dst));
-      if (lane < DSA_MLA_DQK / 64) lds_copy4(row, scl + 4u * lane, lds_addr(dst + DSA_MLA_DQK / 2));
-    }
+    const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
+    if (lane < DSA_MLA_DQK / 32) lds_copy16(row, 16u * lane, lds_addr(dst));
+    if (lane < DSA_MLA_DQK / 64) lds_copy4(row, scl + 4u * lane, lds_addr(dst + DSA_MLA_DQK / 2));
   }
 }
 
