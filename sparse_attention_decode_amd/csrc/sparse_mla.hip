@@ -250,32 +250,45 @@ __device__ __forceinline__ void build_fp8(const Stage& st, const int32_t* rows, 
   }
 }
 
-// NVFP4: decode a stage once into the bf16 token-major tile and the fp16 dim-major tile (E2M1 x
-// E4M3 products are exact in both).
+// NVFP4: decode a stage once into the bf16 token-major tile and the fp16 dim-major tile, one
+// 16-dim block of one token per item.  The hardware converts each pair of E2M1 codes to fp32
+// unscaled (its scaled form does not apply an arbitrary fp32 scale exactly), the block scale
+// multiplies in fp32, and the products (E2M1 x E4M3: at most 6 significant bits, magnitudes in
+// [2^-10, 2688] or 0) are exact in bf16 and fp16, so truncation and round-toward-zero give them
+// exactly.  Tokens that are not selected decode as +0.
 __device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* vt, int tid) {
   for (int it = tid; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
     const int t = it & 31, blk = it >> 5;  // token, 16-dim block
-    float v[16];
-    if (st.valid[t] >= 0) {
-      const uint2 p = *reinterpret_cast<const uint2*>(st.raw + t * kRaw4 + 8 * blk);
-      const float s = fp8_to_f32(st.raw[t * kRaw4 + DSA_MLA_DQK / 2 + blk]);
-      fp4x8_scaled_to_f32x8(p.x, s, v);
-      fp4x8_scaled_to_f32x8(p.y, s, v + 8);
-    } else {
+    const bool ok = st.valid[t] >= 0;
+    uint2 p = *reinterpret_cast<const uint2*>(st.raw + t * kRaw4 + 8 * blk);
+    p = ok ? p : uint2{0u, 0u};  // stale bits of an empty slot become +0 codes
+    const float sc = ok ? fp8_to_f32(st.raw[t * kRaw4 + DSA_MLA_DQK / 2 + blk]) : 1.f;
+    // byte b of each word holds codes 2b (low nibble) and 2b + 1
+    const v2f c[8] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.x, 1.0f, 0),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.x, 1.0f, 1),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.x, 1.0f, 2),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.x, 1.0f, 3),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.y, 1.0f, 0),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.y, 1.0f, 1),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.y, 1.0f, 2),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p.y, 1.0f, 3)};
+    uint32_t w[8], h[8];  // bf16 and fp16 pairs (dims 2j, 2j + 1)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const float a = c[j][0] * sc, b = c[j][1] * sc;
+      w[j] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
     }
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
     uint4* crow = reinterpret_cast<uint4*>(ct + t * kCt4 + 32 * blk);
     crow[0] = uint4{w[0], w[1], w[2], w[3]};
     crow[1] = uint4{w[4], w[5], w[6], w[7]};
     if (16 * blk < DSA_MLA_DV) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        *reinterpret_cast<uint16_t*>(vt + (16 * blk + i) * kVt4 + 2 * t) = (uint16_t)f16_bits(v[i]);
+      for (int j = 0; j < 8; ++j) {
+        uint8_t* row = vt + (16 * blk + 2 * j) * kVt4 + 2 * t;
+        *reinterpret_cast<uint16_t*>(row) = (uint16_t)h[j];
+        *reinterpret_cast<uint16_t*>(row + kVt4) = (uint16_t)(h[j] >> 16);
+      }
     }
   }
 }
