@@ -72,28 +72,6 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// 4 packed E4M3 bytes -> 4 fp32 (exact).
-__device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float* f) {
-  v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  f[0] = lo[0];
-  f[1] = lo[1];
-  f[2] = hi[0];
-  f[3] = hi[1];
-}
-
-// 8 packed E2M1 nibbles (element 2j in the low nibble of byte j) times a block scale -> fp32.
-__device__ __forceinline__ void fp4x8_scaled_to_f32x8(uint32_t w, float s, float* f) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t n = (w >> (4 * j)) & 0xFu;
-    uint32_t e = (n >> 1) & 3u, m = n & 1u;
-    // E2M1: normal 2^(e-1) * (1 + m/2); subnormal (e = 0) m * 0.5
-    float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-    f[j] = ((n & 8u) ? -mag : mag) * s;
-  }
-}
-
 // E4M3 byte -> fp32.
 __device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0];
