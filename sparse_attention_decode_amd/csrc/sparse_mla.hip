@@ -764,7 +764,8 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 // (oc, lane) takes register octet oc of the attention wave blockIdx.y, i.e. head
 // 32 (wave / 4) + lane % 32 and dims 128 (wave % 4) + 32 (oc / 2) + 16 (oc % 2) + 4 (lane / 32)
 // + {0..3, 8..11}.  Partial loads are 16 contiguous bytes per thread (8 KB per workgroup and split).
-// G: splits per group (4, 8 or 16), the smallest that covers nsplit when it can.
+// G: splits per group (4, 8, 16 or 32), the smallest that covers nsplit when it can (16 beyond
+// 32 splits: the 32-split group's registers cost more than its saved round trips there).
 template <int G>
 __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
   const int row = blockIdx.x;
@@ -882,8 +883,10 @@ hipError_t launch_mla_combine(const MlaArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
   else if (a.split_slots <= 8)
     hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(512), 0, s, a);
-  else
+  else if (a.split_slots <= 16 || a.split_slots > 32)  // more slots: groups of 16 measured faster
     hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<32>, cgrid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
