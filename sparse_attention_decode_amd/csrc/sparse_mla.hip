@@ -36,8 +36,10 @@
 //         largest logit and leaves them (fp16, times the token scale), that maximum and their
 //         sum in LDS; every wave of the group then reads all four, takes the tile maximum, and
 //         rescales each quarter's probabilities to the row's running maximum as it loads them.
-//   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  V^T comes from a dim-major fp16 copy of the
-//         value dims, converted once per tile for all head groups.
+//   PV:   O^T[dims x heads] = V^T P^T on fp16 MFMA.  The rows of V^T are read from token-major
+//         tiles with the LDS transpose reads (8 tokens of one dim per lane): FP8 from the
+//         gathered stage itself, converted to fp16 in registers (exact), NVFP4 from the fp16
+//         value tile its decode writes beside the bf16 one.
 // Per-token scales stay out of the MFMA operands (they multiply the logits and the
 // probabilities), so every operand is an exact conversion of the stored codes.  fp16 for P keeps
 // its rounding well inside the output tolerance.  Softmax is online, in base 2.  With S^T and
@@ -50,6 +52,10 @@ namespace dsa {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int lds_v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) lds_v2i_t lds_v2i;
+typedef short lds_v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lds_v4s_t lds_v4s;
 
 constexpr int kHeadGroups = DSA_MLA_HEADS / 32;   // 3 groups of 32 heads
 constexpr int kQuarters = 4;                       // waves per head group
@@ -96,13 +102,14 @@ static_assert(kGatherWaves8 * kWaveChunks8 * 16 <= kSlots * kRaw8, "FP8 gathers 
 // NVFP4 latents
 constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
 constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords; rows 16-byte aligned)
-constexpr int kVt4 = 80;     // fp16 dim-major row bytes (both formats): 64 + pad (20 dwords)
+constexpr int kHt4 = 1056;   // fp16 token-major row bytes of the value dims: 1024 + pad (264
+                              // dwords: the four rows one transpose read meets sit in distinct banks)
 
 template <int LFMT>
 struct Geo {
   static constexpr bool kFp8 = LFMT == DSA_LATENT_FP8;
   static constexpr int kRaw = kFp8 ? kRaw8 : kRaw4;
-  static constexpr int kVt = kVt4;
+  static constexpr int kHtBytes = kFp8 ? 16 : kTile * kHt4;  // fp16 value tile (NVFP4 only)
   static constexpr int kCtBytes = kFp8 ? 16 : kTile * kCt4;  // decoded tile (NVFP4 only)
 };
 
@@ -215,48 +222,28 @@ __device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src
   }
 }
 
-// FP8: dim-major fp16 copy of the value dims of a stage, converted once per tile for all head
-// groups (fp8 -> fp16 is exact).  A thread takes a block of 4 dims x 4 tokens: two conversions
-// per token give its four values as two half-word pairs, and half-word permutes transpose them
-// into four dim rows of 4 tokens.  Tokens that are not selected get zeros, so their (zero)
-// probabilities never meet stale data.
-__device__ __forceinline__ void build_fp8(const Stage& st, const int32_t* rows, uint8_t* vt, int tid) {
-  // the tokens' scales, gathered into each row's pad, side by side for the softmax
+// FP8: the tokens' scales, gathered into each row's pad, side by side for the softmax; and, in a
+// tile with rows that hold no token (rare: the end of a split, or entries with no visible token),
+// the value bytes of those rows cleared, so that PV, which reads the stage itself, multiplies
+// their zero probabilities by zeros and never by stale codes (an E4M3 NaN would survive a zero
+// probability).  `bad`: the wave-uniform ballot of the tile's rows without a token.
+__device__ __forceinline__ void prep_fp8(const Stage& st, const int32_t* rows, uint64_t bad, int tid) {
   if (tid < kTile) st.tsc[tid] = *reinterpret_cast<const float*>(st.raw + tid * kRaw8 + DSA_MLA_DQK);
-  for (int blk = tid; blk < (DSA_MLA_DV / 4) * (kTile / 4); blk += kThreadsM) {
-    const int tq = blk & 7, db = blk >> 3;  // token quad, 4-dim block
-    // the four tokens' pool rows in one read (>= 0: a token); every row read unconditionally,
-    // then selected
-    const int4 ok = *reinterpret_cast<const int4*>(rows + 4 * tq);
-    const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
-    uint32_t lo[4], hi[4];  // token u: fp16 of dims (4db, 4db+1) and of (4db+2, 4db+3)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t r = *reinterpret_cast<const uint32_t*>(st.raw + (4 * tq + u) * kRaw8 + 4 * db);
-      r = okv[u] >= 0 ? r : 0u;
-      lo[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, false));
-      hi[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r, 1.0f, true));
-    }
-    // dim row 4db+i: tokens 4 tq .. 4 tq + 3
-    uint8_t* row = vt + 4 * db * kVt4 + 8 * tq;
-    *reinterpret_cast<uint2*>(row) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u),
-                                           __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)};
-    *reinterpret_cast<uint2*>(row + kVt4) = uint2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
-                                                  __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)};
-    *reinterpret_cast<uint2*>(row + 2 * kVt4) = uint2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u),
-                                                      __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
-    *reinterpret_cast<uint2*>(row + 3 * kVt4) = uint2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
-                                                      __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)};
+  if (bad == 0) return;
+  constexpr int kParts = DSA_MLA_DV / 16;  // 16-byte pieces of a row's value dims
+  for (int it = tid; it < kTile * kParts; it += kThreadsM) {
+    const int t = it / kParts, part = it % kParts;
+    if (rows[t] < 0) *reinterpret_cast<uint4*>(st.raw + t * kRaw8 + 16 * part) = uint4{0u, 0u, 0u, 0u};
   }
 }
 
-// NVFP4: decode a stage once into the bf16 token-major tile and the fp16 dim-major tile, one
-// 16-dim block of one token per item.  The hardware converts each pair of E2M1 codes to fp32
+// NVFP4: decode a stage once into the bf16 tile (all 576 dims) and the fp16 tile (the 512 value
+// dims), both token-major, one 16-dim block of one token per item.  The hardware converts each pair of E2M1 codes to fp32
 // unscaled (its scaled form does not apply an arbitrary fp32 scale exactly), the block scale
 // multiplies in fp32, and the products (E2M1 x E4M3: at most 6 significant bits, magnitudes in
 // [2^-10, 2688] or 0) are exact in bf16 and fp16, so truncation and round-toward-zero give them
 // exactly.  Tokens that are not selected decode as +0.
-__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* vt, int tid) {
+__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* ht, int tid) {
   for (int it = tid; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
     const int t = it & 31, blk = it >> 5;  // token, 16-dim block
     const bool ok = st.valid[t] >= 0;
@@ -283,12 +270,9 @@ __device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_
     crow[0] = uint4{w[0], w[1], w[2], w[3]};
     crow[1] = uint4{w[4], w[5], w[6], w[7]};
     if (16 * blk < DSA_MLA_DV) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint8_t* row = vt + (16 * blk + 2 * j) * kVt4 + 2 * t;
-        *reinterpret_cast<uint16_t*>(row) = (uint16_t)h[j];
-        *reinterpret_cast<uint16_t*>(row + kVt4) = (uint16_t)(h[j] >> 16);
-      }
+      uint4* hrow = reinterpret_cast<uint4*>(ht + t * kHt4 + 32 * blk);
+      hrow[0] = uint4{h[0], h[1], h[2], h[3]};
+      hrow[1] = uint4{h[4], h[5], h[6], h[7]};
     }
   }
 }
@@ -322,9 +306,30 @@ __device__ __forceinline__ v8bf qk_operand(const Stage& st, const uint8_t* ct, i
   }
 }
 
-// Dim-major fp16 value tile as the A operand of PV: dim row d, tokens [t0, t0 + 8).
-__device__ __forceinline__ v8h pv_operand(const uint8_t* vt, int d, int t0) {
-  return __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(vt + d * kVt4 + 2 * t0));
+// NVFP4: the A operand of PV read from the token-major fp16 value tile by two LDS transpose
+// reads.  In each group of 16 lanes a read takes 8 bytes (4 dims) from the address of every lane
+// and hands lane i half-word i % 4 of the pieces of lanes 4r + i / 4, r = 0..3, as its element r.
+// So lane 4r + q of the group points at token t0 + r, dims [d0 + 4q, +4), and lane i receives
+// dim d0 + i of tokens t0 .. t0 + 3; the second read (4 rows further) gives tokens t0 + 4 .. + 7.
+__device__ __forceinline__ v8h pv_operand_f16(const uint8_t* p) {
+  const lds_v4s_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+  const lds_v4s_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * kHt4));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(v8h, v8s{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+}
+
+// FP8: the A operand of PV read from the token-major stage itself by the LDS transpose read.  In
+// each group of 16 lanes the read takes an 8-byte piece from the address of every lane and hands
+// lane i byte i % 8 of the pieces of lanes 2r + i / 8, r = 0..7, as its byte r.  So lane 2r + h of
+// the group points at token t0 + r, dims [d0 + 8h, +8), and lane i receives dim d0 + i of tokens
+// t0 .. t0 + 7: its row of V^T for one K step.  fp8 -> fp16 is exact.
+__device__ __forceinline__ v8h pv_operand_fp8(const uint8_t* p) {
+  const lds_v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+  const uint4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[0], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[0], 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[1], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[1], 1.0f, true))};
+  return __builtin_bit_cast(v8h, r);
 }
 
 // 32x32x16 MFMAs (bf16 for QK, fp16 for PV).  A lane l: row l % 32, K [8 (l / 32), +8); B lane l:
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   constexpr int kValid = G::kFp8 ? 4 : kTile;  // NVFP4 row flags (FP8 takes them from plist)
   __shared__ __attribute__((aligned(16))) int32_t valid0[kValid], valid1[kValid], valid2[kValid],
       valid3[kValid], valid4[kValid], valid5[kValid];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[DSA_MLA_DV * G::kVt];
+  __shared__ __attribute__((aligned(16))) uint8_t ht[G::kHtBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
   // partial S^T exchange: [head group][token quarter][source quarter, own one skipped][lane]
   __shared__ __attribute__((aligned(16))) v4f sx[kHeadGroups][kQuarters][kQuarters - 1][kWave];
@@ -547,9 +552,9 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       const int ln = tl & 63, nl = ln & 31, hl = ln >> 5;
       const int32_t* rows = G::kFp8 ? plist + (j - j0) : cur.valid;  // >= 0: a token
       if constexpr (G::kFp8)
-        build_fp8(cur, rows, vt, tl);
+        prep_fp8(cur, rows, __ballot(rows[nl] < 0), tl);
       else
-        build_nvfp4(cur, ct, vt, tl);
+        build_nvfp4(cur, ct, ht, tl);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
       // this wave's quarter of S^T (32 tokens x the group's 32 heads)
@@ -660,9 +665,23 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const _Float16 f = (_Float16)(hl ? fq[2 * ks + 1] : fq[2 * ks]);
         const v8h p = pf[ks] * f;
+        if constexpr (G::kFp8) {
+          // lane (group g = ln / 16, j = ln % 16): token 16 ks + 8 hl + j / 2, dims
+          // 128 qt + 32 dt + 16 (g % 2) + 8 (j % 2)
+          const uint8_t* vb = cur.raw + (16 * ks + 8 * hl + ((ln & 15) >> 1)) * kRaw8 + 128 * qt +
+                              16 * ((ln >> 4) & 1) + 8 * (ln & 1);
 #pragma unroll
-        for (int dt = 0; dt < kDvTiles; ++dt)
-          o[dt] = mfma32_f16(pv_operand(vt, 128 * qt + 32 * dt + nl, 16 * ks + 8 * hl), p, o[dt]);
+          for (int dt = 0; dt < kDvTiles; ++dt)
+            o[dt] = mfma32_f16(pv_operand_fp8(vb + 32 * dt), p, o[dt]);
+        } else {
+          // lane (group g = ln / 16, j = ln % 16): token 16 ks + 8 hl + j / 4 (and 4 rows on),
+          // dims 128 qt + 32 dt + 16 (g % 2) + 4 (j % 4)
+          const uint8_t* vb = ht + (16 * ks + 8 * hl + ((ln & 15) >> 2)) * kHt4 +
+                              2 * (128 * qt + 16 * ((ln >> 4) & 1) + 4 * (ln & 3));
+#pragma unroll
+          for (int dt = 0; dt < kDvTiles; ++dt)
+            o[dt] = mfma32_f16(pv_operand_f16(vb + 64 * dt), p, o[dt]);
+        }
       }
 
       // Gathers of tile j + kAhead into the stage tile j - 1 used (every wave passed this tile's
