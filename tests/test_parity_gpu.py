@@ -32,6 +32,21 @@ def test_decode_ragged_lengths_fp8(k):
     check_workload(wl, layer)
 
 
+@pytest.mark.parametrize("lat,phys", [(0, True), (0, False), (1, True)])
+def test_attention_never_reads_poisoned_rows_into_the_output(lat, phys):
+    # Nearly the whole pool is spare blocks filled with 0xFF bytes (an E4M3 NaN code), and so are
+    # the slots past each sequence's end.  Tiles that end part-way (visible tokens not a multiple of
+    # 32) gather such rows into their unused slots; a NaN there must never reach the output, even
+    # though its probability is zero.
+    print(f"\n[case] poisoned pool lat={lat} phys={phys}", flush=True)
+    kw = dict(lat_fmt=1, lat_tensor_scale=0.75) if lat else {}
+    wl = _one_row_per_seq(f"poison{lat}{int(phys)}", 47 + lat, [700, 1500, 70, 2100], k=2048,
+                          spare_blocks=1000, **kw)
+    layer, _, _ = run_gpu(wl, phys=phys)
+    assert bool(torch.isfinite(layer.out.float()).all()) and bool(torch.isfinite(layer.lse).all())
+    check_workload(wl, layer)
+
+
 def test_decode_without_scorer_histogram():
     wl = _one_row_per_seq("nohist", 42, [3000, 70000, 129])
     layer, _, _ = run_gpu(wl, use_hist=False)
