@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
         if (rho != qt)
           sx[hg][rho][qt < rho ? qt : qt - 1][ln] =
               v4f{acc[4 * rho], acc[4 * rho + 1], acc[4 * rho + 2], acc[4 * rho + 3]};
-      lds_barrier();  // partial S^T of every quarter, and the value tile, are in LDS
+      lds_barrier();  // partial S^T of every quarter (and FP8's cleared rows) are in LDS
 
       // S^T of this wave's token quarter: tokens 8 qt + 4 hl + i, head nl; the four partials
       // are added in quarter order
