@@ -787,9 +787,12 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
 // 32 splits: the 32-split group's registers cost more than its saved round trips there).
 template <int G>
 __global__ __launch_bounds__(512) void mla_combine_kernel(MlaArgs a) {
+  // 96 slots per row (attention wave, register octet), blockDim.x / 64 of them per workgroup: a
+  // batch of few rows takes small workgroups, so that its loads are spread over many CUs
   const int row = blockIdx.x;
-  const int wave = blockIdx.y;
-  const int oc = threadIdx.x >> 6;
+  const int slot = blockIdx.y * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+  const int wave = slot >> 3;
+  const int oc = slot & 7;
   const int lane = threadIdx.x & 63;
   const int head = 32 * (wave >> 2) + (lane & 31);
   const int d = 128 * (wave & 3) + 32 * (oc >> 1) + 16 * (oc & 1) + 4 * (lane >> 5);
@@ -895,17 +898,28 @@ size_t mla_workspace_bytes(int32_t num_rows, int32_t k, bool invariant) {
   return (size_t)num_rows * ns * DSA_MLA_HEADS * (DSA_MLA_DV * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
+#ifndef DSA_COMBINE_ROWS8
+#define DSA_COMBINE_ROWS8 32
+#endif
+#ifndef DSA_COMBINE_ROWS2
+#define DSA_COMBINE_ROWS2 4
+#endif
+constexpr int kCombineRows8 = DSA_COMBINE_ROWS8, kCombineRows2 = DSA_COMBINE_ROWS2;
+
 hipError_t launch_mla_combine(const MlaArgs& a, hipStream_t s) {
   if (a.batch.num_rows <= 0) return hipSuccess;
-  const dim3 cgrid((unsigned)a.batch.num_rows, kWavesM);
+  // waves per workgroup: 8 (one attention wave's 8 octets) from 32 rows on, fewer below
+  const int rows = a.batch.num_rows;
+  const int wpg = rows >= kCombineRows8 ? 8 : rows >= kCombineRows2 ? 2 : 1;
+  const dim3 cgrid((unsigned)rows, (unsigned)(kWavesM * 8 / wpg)), cblock((unsigned)(kWave * wpg));
   if (a.split_slots <= 4)
-    hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, s, a);
   else if (a.split_slots <= 8)
-    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, s, a);
   else if (a.split_slots <= 16 || a.split_slots > 32)  // more slots: groups of 16 measured faster
-    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, cblock, 0, s, a);
   else
-    hipLaunchKernelGGL(mla_combine_kernel<32>, cgrid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(mla_combine_kernel<32>, cgrid, cblock, 0, s, a);
   return hipGetLastError();
 }
 
