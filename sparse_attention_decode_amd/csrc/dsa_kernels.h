@@ -90,6 +90,7 @@ struct TopkArgs {
   int64_t cand_ld;
   int32_t num_slices;
   int32_t vec_ok;       // scores rows are 16-byte aligned
+  int32_t max_n;        // the batch's bound on visible tokens per row (direct select: reads stop there)
   const uint32_t* status;  // the device status word: a row-count violation poisons the select
 };
 size_t topk_workspace_bytes(int32_t num_rows, int64_t max_context);

@@ -32,6 +32,9 @@ constexpr int kLevel1Slices = 64;
 constexpr int kResolveThreads = 1024;
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kCap = 8192;  // survivors resolved in LDS
+// Batches whose rows see at most kCap tokens skip the filter: the resolve reads each row's scores
+// itself, kDirectPer per thread.
+constexpr int kDirectPer = kCap / kResolveThreads;
 
 __device__ __forceinline__ int row_seq(const BatchView& b, int row) {
   int lo = 0, hi = b.num_seqs - 1;
@@ -247,6 +250,8 @@ struct ResolveShared {
   uint32_t wtot[kResolveWaves];
 };
 
+// DIRECT: rows of at most kCap visible tokens, no filter pass before (see kDirectPer).
+template <bool DIRECT>
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs a) {
   __shared__ ResolveShared sh;
   const int row = blockIdx.x;
@@ -287,13 +292,56 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     const int i = tid + kResolveThreads * j;
     btv[j] = (bt_cached && i < nblk) ? bt[i] : 0;
   }
-  const int nsl = (n + kTopkSlice - 1) / kTopkSlice;
-  // level 1 (the top 11 key bits) was resolved by the filter from the histogram
-  const uint32_t b1 = a.level1[2 * row];
-  uint32_t need = a.level1[2 * row + 1];
-
-  // survivors per slice -> exclusive prefix
-  {
+  const int nsl = DIRECT ? 0 : (n + kTopkSlice - 1) / kTopkSlice;
+  uint32_t b1, need, M;
+  if constexpr (DIRECT) {
+    // The row's scores (kDirectPer consecutive tokens per thread) and its histogram are read at
+    // once; level 1 (the top 11 key bits) comes from the histogram, and the keys in the threshold
+    // bin or above are compacted into LDS in token order, as the filter would have left them.
+    const int nr = min(n, a.max_n);  // max_n <= kCap
+    const int t0 = kDirectPer * tid;
+    const float* src = a.scores + (int64_t)row * a.ld + t0;
+    float v[kDirectPer];
+    if (t0 + kDirectPer <= nr && a.vec_ok) {
+#pragma unroll
+      for (int j = 0; j < kDirectPer; j += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(src + j);
+        v[j] = f.x; v[j + 1] = f.y; v[j + 2] = f.z; v[j + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDirectPer; ++j) v[j] = (t0 + j < nr) ? src[j] : 0.f;
+    }
+    uint32_t hv[kBins / kResolveThreads];
+#pragma unroll
+    for (int j = 0; j < kBins / kResolveThreads; ++j) hv[j] = hist_row[tid + kResolveThreads * j];
+#pragma unroll
+    for (int j = 0; j < kBins / kResolveThreads; ++j) sh.hist[tid + kResolveThreads * j] = hv[j];
+    __syncthreads();
+    uint32_t rest;
+    b1 = select_bin<kResolveThreads>(sh.hist, kBins, (uint32_t)k, &rest, sh.sc, sh.wtot);
+    need = rest;
+    uint32_t keep = 0, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kDirectPer; ++j) {
+      const bool in = t0 + j < nr && (order_key(v[j]) >> 21) >= b1;
+      keep |= in ? (1u << j) : 0u;
+      cnt += in ? 1u : 0u;
+    }
+    uint32_t pos = block_excl_scan<kResolveThreads>(cnt, &M, sh.wtot);
+#pragma unroll
+    for (int j = 0; j < kDirectPer; ++j)
+      if (keep & (1u << j)) {
+        sh.key[pos] = order_key(v[j]);
+        sh.idx[pos] = t0 + j;
+        ++pos;
+      }
+    __syncthreads();
+  } else {
+    // level 1 (the top 11 key bits) was resolved by the filter from the histogram
+    b1 = a.level1[2 * row];
+    need = a.level1[2 * row + 1];
+    // survivors per slice -> exclusive prefix
     const uint32_t* cnt = a.slice_cnt + (int64_t)row * a.num_slices;
     uint32_t carry = 0;
     for (int s0 = 0; s0 < nsl; s0 += kResolveThreads) {
@@ -305,9 +353,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     }
     if (tid == 0) sh.pre[nsl] = carry;
     __syncthreads();
+    M = sh.pre[nsl];
   }
-  const uint32_t M = sh.pre[nsl];
-  const bool in_lds = M <= (uint32_t)kCap;
+  const bool in_lds = DIRECT || M <= (uint32_t)kCap;
   const uint2* cand = a.cand + (int64_t)row * a.cand_ld;
   // survivor e (in token order) -> (key, token index)
   auto cand_at = [&](uint32_t e) -> uint2 {
@@ -318,7 +366,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkArgs 
     }
     return cand[lo * kTopkSlice + (int)(e - sh.pre[lo])];
   };
-  if (in_lds) {  // survivors in batches of 4 per thread, every load of a batch in flight at once
+  if (!DIRECT && in_lds) {  // survivors in batches of 4 per thread, every load of a batch in flight at once
     constexpr int kPer = 4;
     for (uint32_t e0 = 0; e0 < M; e0 += kPer * kResolveThreads) {
       uint2 kv[kPer];
@@ -452,6 +500,8 @@ hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStr
   cand += ((uintptr_t)cand & 7) ? 1 : 0;  // 8-byte alignment of the (key, index) pairs
   a.cand = reinterpret_cast<uint2*>(cand);
   a.vec_ok = ((a.ld & 3) == 0) && ((((uintptr_t)a.scores) & 15) == 0);
+  a.max_n = (int32_t)std::min<int64_t>(max_context, kCap);
+  const bool direct = max_context <= kCap;  // every row's survivors fit in LDS: no filter pass
   hipError_t e;
   if (a.hist_in == nullptr) {
     if ((e = launch_zero_u32(hist_ws, R * kBins, s)) != hipSuccess) return e;
@@ -459,6 +509,10 @@ hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStr
     hipLaunchKernelGGL(topk_hist_kernel, gh, dim3(256), 0, s, a, hist_ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     a.hist_in = hist_ws;
+  }
+  if (direct) {
+    hipLaunchKernelGGL(topk_resolve_kernel<true>, dim3((unsigned)R), dim3(kResolveThreads), 0, s, a);
+    return hipGetLastError();
   }
   const bool l1 = a.num_slices > kLevel1Slices;  // many slices per row: find each row's bin once
   if (l1) {
@@ -472,7 +526,7 @@ hipError_t launch_topk(const TopkArgs& a0, int64_t max_context, void* ws, hipStr
     hipLaunchKernelGGL(topk_filter_kernel<false>, dim3((unsigned)a.num_slices, (unsigned)R),
                        dim3(kFilterThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3((unsigned)R), dim3(kResolveThreads), 0, s, a);
+  hipLaunchKernelGGL(topk_resolve_kernel<false>, dim3((unsigned)R), dim3(kResolveThreads), 0, s, a);
   return hipGetLastError();
 }
 

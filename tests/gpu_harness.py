@@ -14,17 +14,27 @@ RTOL, ATOL = 2e-2, 2e-3  # bf16 outputs and fp32 log-sum-exp against the float64
 
 
 def run_gpu(wl: synth.Workload, use_hist=None, prefill=None, zero_qidx=False, phys=True, flags=0,
-            candidates=False, pool_edit=None):
+            candidates=False, pool_edit=None, context_bound=None):
     """Run the layer through the C ABI on workload wl.  candidates: scores are never stored (the
-    candidates path); pool_edit(pool, kv): a change made to the staged pool before the run."""
+    candidates path); pool_edit(pool, kv): a change made to the staged pool before the run;
+    context_bound: a larger bound on the rows' visible tokens than the batch's own (the block table
+    is padded with -1 to match), which only changes how the library sizes its passes."""
     kv = sad.kv_layout(wl.ikey_fmt, wl.lat_fmt, wl.num_blocks, wl.lat_tensor_scale)
     d = synth.device.stage(wl, kv.as_dict())
     if zero_qidx:
         d["q_idx"].zero_()
     if pool_edit is not None:
         pool_edit(d["pool"], kv)
-    batch = sad.DeviceBatch(d["block_table"], d["seq_row_start"], d["row_pos"],
-                            d["max_rows_per_seq"], d["max_context"], flags)
+    bt, max_context = d["block_table"], d["max_context"]
+    if context_bound is not None:
+        assert context_bound >= max_context
+        nb = (context_bound + 63) // 64
+        if nb > bt.shape[1]:
+            pad = torch.full((bt.shape[0], nb - bt.shape[1]), -1, dtype=bt.dtype, device=bt.device)
+            bt = torch.cat([bt, pad], dim=1).contiguous()
+        max_context = context_bound
+    batch = sad.DeviceBatch(bt, d["seq_row_start"], d["row_pos"], d["max_rows_per_seq"],
+                            max_context, flags)
     if prefill is None:
         prefill = d["max_rows_per_seq"] > sad.MAX_ROWS_PER_SEQ
     layer = sad.DSALayer(kv, batch, wl.k, wl.softmax_scale, prefill=prefill, use_hist=use_hist,

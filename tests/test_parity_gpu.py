@@ -47,6 +47,32 @@ def test_attention_never_reads_poisoned_rows_into_the_output(lat, phys):
     check_workload(wl, layer)
 
 
+@pytest.mark.parametrize("k", [2048, 100, 7, 1])
+def test_short_rows_select_in_one_pass(k):
+    # Every row sees at most 8,192 tokens, so the select reads the scores in its resolve pass and
+    # runs no filter; the same rows under a context bound of 8,193 take the filter path.  Both
+    # against the oracle, and bit-identical to each other.
+    print(f"\n[case] short rows k={k}", flush=True)
+    wl = _one_row_per_seq(f"short{k}", 60 + k, [1, 63, 65, 2047, 2049, 5000, 8191, 8192], k=k)
+    direct, _, _ = run_gpu(wl)
+    check_workload(wl, direct)
+    filtered, _, _ = run_gpu(wl, context_bound=8193)
+    assert torch.equal(direct.count, filtered.count)
+    assert torch.equal(direct.idx, filtered.idx)
+    assert torch.equal(direct.phys, filtered.phys)
+    assert torch.equal(direct.out.view(torch.int16), filtered.out.view(torch.int16))
+
+
+def test_short_rows_all_scores_tied():
+    # q = 0 on rows of at most 8,192 tokens: every key ties, and the lowest indices are selected
+    print("\n[case] short rows all tied", flush=True)
+    wl = _one_row_per_seq("shortties", 71, [3000, 8192, 2100])
+    layer, _, _ = run_gpu(wl, zero_qidx=True)
+    check_workload(wl, layer, zero_qidx=True)
+    idx = layer.idx.cpu().numpy()
+    assert np.array_equal(idx[0], np.arange(2048)) and np.array_equal(idx[1], np.arange(2048))
+
+
 def test_decode_without_scorer_histogram():
     wl = _one_row_per_seq("nohist", 42, [3000, 70000, 129])
     layer, _, _ = run_gpu(wl, use_hist=False)
