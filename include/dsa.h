@@ -90,8 +90,11 @@ enum {
  *                         key scale    [bs] fp32 (> 0)       at ikey_scale_off
  *   ikey_format MXFP4:    keys         [bs][64] packed E2M1  at ikey_off
  *                         block scales [bs][4] E8M0 (one per 32 elements) at ikey_scale_off
- * row_bytes is a multiple of 256.  Token s of a sequence lives in row block_table[s / bs],
- * slot s % bs; its physical row index is block_table[s / bs] * bs + s % bs.
+ * row_bytes is a multiple of 256, and every page lies inside the row; the latent-scale page must
+ * also have at least 12 bytes of the row behind it (the attention copies a token's latent scales
+ * as whole 16-byte pieces).  Entry points reject a layout that breaks these rules with
+ * DSA_ERR_INVALID_ARG; dsa_kv_layout_init always meets them.  Token s of a sequence lives in row
+ * block_table[s / bs], slot s % bs; its physical row index is block_table[s / bs] * bs + s % bs.
  */
 typedef struct dsa_kv_layout {
   int32_t block_size;    /* tokens per block; this build supports 64 */

@@ -126,6 +126,22 @@ dsa_status check_layout(const dsa_kv_layout* kv, const void* pool) {
   if (kv->row_bytes <= 0 || kv->row_bytes % 256)
     return fail(DSA_ERR_INVALID_ARG, "row_bytes %lld must be a positive multiple of 256",
                 (long long)kv->row_bytes);
+  {
+    // every page inside the row; the attention gathers a token's latent scales as whole 16-byte
+    // pieces, reading up to 12 bytes past its scales, so the latent-scale page needs 12 bytes of
+    // the row behind it
+    const bool fp8l = kv->latent_format == DSA_LATENT_FP8, fp8k = kv->ikey_format == DSA_IKEY_FP8;
+    const int64_t bs = kv->block_size;
+    const int64_t ends[4] = {kv->latent_off + bs * (fp8l ? DSA_MLA_DQK : DSA_MLA_DQK / 2),
+                             kv->latent_scale_off + bs * (fp8l ? 4 : DSA_MLA_DQK / 16) + 12,
+                             kv->ikey_off + bs * (fp8k ? DSA_INDEX_DIM : DSA_INDEX_DIM / 2),
+                             kv->ikey_scale_off + bs * (fp8k ? 4 : DSA_INDEX_DIM / 32)};
+    for (int i = 0; i < 4; ++i)
+      if (ends[i] > kv->row_bytes)
+        return fail(DSA_ERR_INVALID_ARG, "page at offset %lld extends past row_bytes %lld%s",
+                    (long long)offs[i], (long long)kv->row_bytes,
+                    i == 1 ? " (the latent scales need 12 bytes of the row behind them)" : "");
+  }
   if (kv->num_blocks <= 0) return fail(DSA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (kv->latent_format == DSA_LATENT_NVFP4 &&
       !(kv->latent_tensor_scale > 0.f && isfinite(kv->latent_tensor_scale)))

@@ -56,6 +56,28 @@ def test_layout_rejects_bad_arguments():
         sad.kv_layout(sad.IKEY_FP8, sad.LATENT_NVFP4, 10, 0.0)
 
 
+def test_layout_pages_must_fit_in_the_row():
+    # a hand-made layout whose latent-scale page sits at the very end of the row: the attention's
+    # 16-byte scale gathers would read past it, so every entry point rejects the layout
+    lib = L.lib()
+    b = _fake_batch()
+    p = ctypes.c_void_p(0x2000)
+    for ikey, lat in ((sad.IKEY_FP8, sad.LATENT_FP8), (sad.IKEY_MXFP4, sad.LATENT_NVFP4)):
+        kv = sad.kv_layout(ikey, lat, 10, 0.5 if lat else 1.0)
+        scale_bytes = 64 * (4 if lat == sad.LATENT_FP8 else 36)
+        kv.latent_off, kv.latent_scale_off, kv.ikey_off, kv.ikey_scale_off = (
+            0, kv.row_bytes - (scale_bytes + 15) // 16 * 16, kv.latent_scale_off, kv.ikey_off)
+        assert lib.dsa_indexer_scores(ctypes.byref(kv), ctypes.c_void_p(0x100000), ctypes.byref(b),
+                                      p, p, p, 128, None, None) == L.DSA_ERR_INVALID_ARG
+        assert b"12 bytes" in lib.dsa_last_error()
+        # a page running past the row
+        kv2 = sad.kv_layout(ikey, lat, 10, 0.5 if lat else 1.0)
+        kv2.ikey_off = kv2.row_bytes - 16
+        assert lib.dsa_indexer_scores(ctypes.byref(kv2), ctypes.c_void_p(0x100000), ctypes.byref(b),
+                                      p, p, p, 128, None, None) == L.DSA_ERR_INVALID_ARG
+        assert b"extends past" in lib.dsa_last_error()
+
+
 def _fake_batch(**over):
     b = L.Batch()
     b.num_seqs, b.num_rows, b.max_rows_per_seq, b.max_blocks_per_seq = 1, 1, 1, 2
