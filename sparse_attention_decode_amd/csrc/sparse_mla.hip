@@ -22,11 +22,10 @@
 // gathered from the paged pool straight into LDS with direct global->LDS loads (no registers
 // held in flight), kStages - 1 tiles ahead of the tile being processed.  Each stage is its own
 // LDS variable and barriers wait on LDS traffic only, so reading a tile never waits for the
-// gathers of later tiles.  FP8: the split's pool rows are resolved once into an LDS list, and a
-// tile is gathered as 16-byte chunks at consecutive LDS addresses, two full 64-lane gathers per
-// wave with a 64-bit address per lane (no per-row scalar work, no exec masking).  NVFP4: the pool
-// rows to gather are handed over in a lane-distributed register (one batch of 21 tiles per
-// register) and read with readlane, one latent and one scale gather per row.
+// gathers of later tiles.  The split's pool rows are resolved once into an LDS list, and a tile
+// is gathered as 16-byte chunks at consecutive LDS addresses, full 64-lane gathers with a 64-bit
+// address per lane (FP8: two per wave from 10 waves; NVFP4: one per wave from 11), with no per-row
+// scalar work and no exec masking.
 //   QK^T: S^T[tokens x heads] = C Q^T on bf16 MFMA.  The query stays in registers (B operand);
 //         the latent tile is the A operand.  FP8 latents are read raw from LDS and converted to
 //         bf16 in registers (exact); NVFP4 latents are decoded once per tile into a bf16 tile.
@@ -72,54 +71,55 @@ constexpr int kPsRow = 80;                         // fp16 probability row: 32 t
 constexpr int kStages = DSA_MLA_STAGES;
 constexpr int kAhead = kStages - 1;
 static_assert(kStages >= 3 && kStages <= 6, "stage variables raw0..raw5");
-constexpr int kRowsPerWave = (kTile + kWavesM - 1) / kWavesM;  // 3 (rows >= 32 are dummies)
+constexpr int kRowsPerWave = (kTile + kWavesM - 1) / kWavesM;  // 3 (rows >= 32 are spare)
 constexpr int kSlots = kRowsPerWave * kWavesM;                  // 36 LDS rows per stage
-// Pool rows of a wave's gathers, one register per batch of tiles: lane 3T + r holds the row of
-// tile T's row r of the batch (kBatchTiles tiles per register).
-constexpr int kBatchTiles = kWave / kRowsPerWave;  // 21
-// Every gathering wave issues exactly this many gathers per tile (FP8: two chunk gathers; NVFP4:
-// data + block scales per row, dummies included), so waiting for a tile is "all but the newest
-// tiles' gathers are done".
-template <int LFMT>
-constexpr int kGathersPerWave = LFMT == DSA_LATENT_FP8 ? 2 : 2 * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 4.f;  // base-2 headroom of the running max (probabilities <= 16)
 
 // FP8 latents
 constexpr int kRaw8 = 592;   // raw row bytes: 576 codes + pad (148 dwords: b128 reads conflict-free)
-// FP8 tiles are copied as 16-byte chunks: chunk c of a tile is part c % 37 of row c / 37 (parts
-// 0..35: the 576 latent bytes; part 36: the 16 bytes from the token's scale on, into the row's
-// pad), so the tile is 1,184 chunks at consecutive LDS addresses.  Waves 0..9 copy chunks
-// [128 w, 128 w + 128) in two full 64-lane gathers; the last 96 (past the 32 rows) land in the
-// stage's spare rows.  Waves 10 and 11 copy nothing.
-constexpr int kChunks8 = kRaw8 / 16;                // 37 per row
-constexpr int kTileChunks8 = kTile * kChunks8;      // 1184 per tile
-constexpr int kWaveChunks8 = 2 * kWave;             // 128 per gathering wave
-constexpr int kGatherWaves8 = (kTileChunks8 + kWaveChunks8 - 1) / kWaveChunks8;  // 10
-static_assert(kGatherWaves8 <= kWavesM, "FP8 gathers");
-static_assert(kGatherWaves8 * kWaveChunks8 * 16 <= kSlots * kRaw8, "FP8 gathers stay in the stage");
 // NVFP4 latents
-constexpr int kRaw4 = 336;   // raw row bytes: 288 packed + 36 block scales + pad
+constexpr int kRaw4 = 336;   // raw row bytes: 288 packed codes + 48 (the 36 block scales and 12 past)
 constexpr int kCt4 = 1168;   // bf16 token-major row bytes: 1152 + pad (292 dwords; rows 16-byte aligned)
 constexpr int kHt4 = 1056;   // fp16 token-major row bytes of the value dims: 1024 + pad (264
                               // dwords: the four rows one transpose read meets sit in distinct banks)
 
+// A tile is copied into its stage as 16-byte chunks at consecutive LDS addresses: chunk c is part
+// c % kChunks of row c / kChunks, parts [0, kLatChunks) the token's latent bytes and the rest the
+// 16-byte pieces from its scales on (FP8: one, the 4 scale bytes and 12 past them, into the row's
+// pad; NVFP4: three, the 36 block-scale bytes and 12 past them; the pool layout keeps 12 bytes of
+// the row behind the scale page).  Gathering waves 0 .. kGatherWaves - 1 each issue kGathers full
+// 64-lane copies per tile, chunks [kWaveChunks w, +kWaveChunks); lanes past the tile re-read its
+// last chunk into the stage's spare rows.  Every gathering wave issues the same number of copies
+// per tile, so waiting for a tile is "all but the newest tiles' copies are done".
 template <int LFMT>
 struct Geo {
   static constexpr bool kFp8 = LFMT == DSA_LATENT_FP8;
   static constexpr int kRaw = kFp8 ? kRaw8 : kRaw4;
+  static constexpr int kLatBytes = kFp8 ? DSA_MLA_DQK : DSA_MLA_DQK / 2;  // latent bytes per token
+  static constexpr int kSclBytes = kFp8 ? 4 : DSA_MLA_DQK / 16;           // scale bytes per token
+  static constexpr int kLatChunks = kLatBytes / 16;                       // 36 / 18
+  static constexpr int kChunks = kRaw / 16;                               // 37 / 21 per row
+  static constexpr int kTileChunks = kTile * kChunks;                     // 1184 / 672 per tile
+  static constexpr int kGathers = kFp8 ? 2 : 1;       // copies per gathering wave and tile
+  static constexpr int kWaveChunks = kGathers * kWave;                    // 128 / 64
+  static constexpr int kGatherWaves = (kTileChunks + kWaveChunks - 1) / kWaveChunks;  // 10 / 11
   static constexpr int kHtBytes = kFp8 ? 16 : kTile * kHt4;  // fp16 value tile (NVFP4 only)
   static constexpr int kCtBytes = kFp8 ? 16 : kTile * kCt4;  // decoded tile (NVFP4 only)
+  static_assert(kChunks * 16 == kRaw && kLatChunks * 16 == kLatBytes, "whole chunks");
+  static_assert((kChunks - kLatChunks) * 16 >= kSclBytes &&
+                (kChunks - kLatChunks) * 16 - kSclBytes <= 12, "scale pieces read at most 12 bytes past");
+  static_assert(kGatherWaves <= kWavesM, "gathering waves");
+  static_assert(kGatherWaves * kWaveChunks * 16 <= kSlots * kRaw, "copies stay in the stage");
 };
 
 // One pipeline stage: where a gathered tile lands.  Each stage's buffers are separate
 // __shared__ variables, so the compiler can tell the reads of one stage from the gathers still
 // landing in the others (one shared array would make it wait for every gather before any read).
 struct Stage {
-  uint8_t* raw;    // [kSlots][kRaw] latent rows as stored (rows >= kTile: dummy gathers)
+  uint8_t* raw;    // [kSlots][kRaw] latent rows as stored (rows >= kTile: spare)
   float* tsc;      // [kSlots] FP8 token scales
-  int32_t* valid;  // NVFP4: [kTile] >= 0 where the slot holds a selected, visible token, else -1
 };
 
 // The value of x, opaque to the optimiser: lane-dependent addresses derived from it inside the tile
@@ -130,8 +130,8 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Direct global->LDS copies.  Lane l copies `bytes` bytes from src + voff (src wave-uniform) to LDS
-// address lds + bytes * l.  Issued through inline assembly, so the compiler does not track them:
+// Direct global->LDS copies.  Lane l copies 16 bytes from its own 64-bit address to LDS address
+// lds + 16 l.  Issued through inline assembly, so the compiler does not track them:
 // the tile loop waits for them explicitly (s_waitcnt vmcnt by count, then an LDS barrier).  Left
 // to the compiler, its LDS-DMA tracking made some LDS writes wait for every copy in flight, which
 // undid the gather pipeline.  Untracked copies only ever make the compiler's own waits stricter.
@@ -143,82 +143,36 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // kernels (their ISA has no m0 access but these writes), so setting it here disturbs nothing; it
 // is listed as clobbered, which the compiler notes it cannot promise to honour for m0.
 #define DSA_GATHER_POLICY " nt"
-__device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" DSA_GATHER_POLICY
-               :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" DSA_GATHER_POLICY
-               :: "v"(voff), "s"(src), "s"(lds) : "memory", "m0");
-}
-
-// One chunk gather with a 64-bit address per lane: lane l copies 16 bytes from addr to LDS
-// address lds + 16 l.
 __device__ __forceinline__ void lds_copy16_va(uint64_t addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" DSA_GATHER_POLICY
                :: "v"(addr), "s"(lds) : "memory", "m0");
 }
 
-// FP8: the chunk gathers of one tile into stage st.  rows: the tile's 32 pool rows (-1: no
-// token; such a row gathers pool row `spare` instead, whose data is never used).  Each lane finds
-// its chunk's row in LDS and forms the address itself, so the wave issues two instructions and
-// no per-row scalar work.  Chunks past the tile read row 31's last chunk again.
-__device__ __forceinline__ void issue_tile_fp8(const Stage& st, const int32_t* rows, const MlaArgs& a,
-                                               int wave, int lane, int spare) {
-  if (wave >= kGatherWaves8) return;
+// The chunk gathers of one tile into stage st.  rows: the tile's 32 pool rows (-1: no token; such
+// a row gathers pool row `spare` instead, whose data is never used).  Each lane finds its chunk's
+// row in LDS and forms the address itself, so a gathering wave issues kGathers instructions and no
+// per-row scalar work.
+template <int LFMT>
+__device__ __forceinline__ void issue_tile(const Stage& st, const int32_t* rows, const MlaArgs& a,
+                                           int wave, int lane, int spare) {
+  using G = Geo<LFMT>;
+  if (wave >= G::kGatherWaves) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = min(kWaveChunks8 * wave + kWave * i + lane, kTileChunks8 - 1);
-    const int t = c / kChunks8, part = c - kChunks8 * t;
+  for (int i = 0; i < G::kGathers; ++i) {
+    const int c = min(G::kWaveChunks * wave + kWave * i + lane, G::kTileChunks - 1);
+    const int t = c / G::kChunks, part = c - G::kChunks * t;
     const int ph = rows[t];
     const uint32_t src = (uint32_t)(ph >= 0 ? ph : spare);
     const uint32_t slot = src & (kBlock - 1);
     // offsets inside a pool row fit 32 bits; the latent or the scale offset picked by a mask,
     // not a branch
-    const uint32_t lat = (uint32_t)a.pool.lat_off + slot * DSA_MLA_DQK + 16u * part;
-    const uint32_t scl = (uint32_t)a.pool.lat_scale_off + slot * 4u;
-    const uint32_t within = scl ^ ((lat ^ scl) & (0u - (uint32_t)(part < DSA_MLA_DQK / 16)));
+    const uint32_t lat = (uint32_t)a.pool.lat_off + slot * G::kLatBytes + 16u * part;
+    uint32_t scl = (uint32_t)a.pool.lat_scale_off + slot * G::kSclBytes;
+    if constexpr (G::kChunks - G::kLatChunks > 1) scl += 16u * (uint32_t)(part - G::kLatChunks);
+    const uint32_t within = scl ^ ((lat ^ scl) & (0u - (uint32_t)(part < G::kLatChunks)));
     const uint64_t addr = reinterpret_cast<uint64_t>(a.pool.base) +
                           (uint64_t)(src >> 6) * (uint32_t)a.pool.row_bytes + within;
-    lds_copy16_va(addr, lds_addr(st.raw + 16 * (kWaveChunks8 * wave + kWave * i)));
-  }
-}
-
-// NVFP4: gather sources of one wave for a batch of kBatchTiles tiles, one register set per
-// batch: lane 3T + r holds, for row wave + 12 r of tile T of the batch, the byte offset from the
-// pool base of what that row gathers (its latent, or a dummy row's: see below), bit 63 set when
-// the row holds a selected, visible token, and the offset of the row's block scales from its
-// latent.
-// Everything that depends on the selection is resolved here, once per batch, so issuing a tile's
-// gathers is a few scalar instructions per row.
-struct GatherSrc {
-  uint32_t lo, hi;   // byte offset (bits 0..62) and the valid flag (bit 63)
-  uint32_t scl;      // NVFP4: block scales - latent, in bytes (positive: the scale page follows)
-};
-
-// NVFP4: issue the direct global->LDS gathers of tile T of the current batch into stage st: wave
-// w gathers tile rows w, w+12, w+24 (lanes 3T, 3T+1, 3T+2 of `src`).  Rows past the tile (slots
-// 32..35 of the stage) and slots without a token gather a dummy row, so that every wave issues
-// kGathersPerWave loads per tile.  Every gather lands in the stage's own LDS variable, and its
-// source is wave-uniform (scalar base address, 32-bit lane offset).
-template <int LFMT>
-__device__ __forceinline__ void issue_tile(const Stage& st, const GatherSrc& src, int T,
-                                           const MlaArgs& a, int lane) {
-  using G = Geo<LFMT>;
-  static_assert(!G::kFp8, "FP8 tiles are gathered as chunks (issue_tile_fp8)");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int t = wave + kWavesM * r;  // < kSlots
-    const int l = kRowsPerWave * T + r;
-    const uint32_t lo = __builtin_amdgcn_readlane(src.lo, l);
-    const uint32_t hi = __builtin_amdgcn_readlane(src.hi, l);
-    if (t < kTile && lane == 0) st.valid[t] = (int)(hi >> 31) - 1;
-    const uint8_t* row = a.pool.base + ((((uint64_t)(hi & 0x7FFFFFFFu)) << 32) | lo);
-    uint8_t* dst = st.raw + t * G::kRaw;
-    const uint32_t scl = __builtin_amdgcn_readlane(src.scl, l);
-    if (lane < DSA_MLA_DQK / 32) lds_copy16(row, 16u * lane, lds_addr(dst));
-    if (lane < DSA_MLA_DQK / 64) lds_copy4(row, scl + 4u * lane, lds_addr(dst + DSA_MLA_DQK / 2));
+    lds_copy16_va(addr, lds_addr(st.raw + 16 * (G::kWaveChunks * wave + kWave * i)));
   }
 }
 
@@ -243,10 +197,11 @@ __device__ __forceinline__ void prep_fp8(const Stage& st, const int32_t* rows, u
 // multiplies in fp32, and the products (E2M1 x E4M3: at most 6 significant bits, magnitudes in
 // [2^-10, 2688] or 0) are exact in bf16 and fp16, so truncation and round-toward-zero give them
 // exactly.  Tokens that are not selected decode as +0.
-__device__ __forceinline__ void build_nvfp4(const Stage& st, uint8_t* ct, uint8_t* ht, int tid) {
+__device__ __forceinline__ void build_nvfp4(const Stage& st, const int32_t* rows, uint8_t* ct,
+                                            uint8_t* ht, int tid) {
   for (int it = tid; it < (DSA_MLA_DQK / 16) * kTile; it += kThreadsM) {
     const int t = it & 31, blk = it >> 5;  // token, 16-dim block
-    const bool ok = st.valid[t] >= 0;
+    const bool ok = rows[t] >= 0;
     uint2 p = *reinterpret_cast<const uint2*>(st.raw + t * kRaw4 + 8 * blk);
     p = ok ? p : uint2{0u, 0u};  // stale bits of an empty slot become +0 codes
     const float sc = ok ? fp8_to_f32(st.raw[t * kRaw4 + DSA_MLA_DQK / 2 + blk]) : 1.f;
@@ -354,23 +309,20 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   constexpr int kTsc = G::kFp8 ? kSlots : 4;  // FP8 token scales (NVFP4 has none)
   __shared__ __attribute__((aligned(16))) float tsc0[kTsc], tsc1[kTsc], tsc2[kTsc],
       tsc3[kTsc], tsc4[kTsc], tsc5[kTsc];
-  constexpr int kValid = G::kFp8 ? 4 : kTile;  // NVFP4 row flags (FP8 takes them from plist)
-  __shared__ __attribute__((aligned(16))) int32_t valid0[kValid], valid1[kValid], valid2[kValid],
-      valid3[kValid], valid4[kValid], valid5[kValid];
   __shared__ __attribute__((aligned(16))) uint8_t ht[G::kHtBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ct[G::kCtBytes];
   // partial S^T exchange: [head group][token quarter][source quarter, own one skipped][lane]
   __shared__ __attribute__((aligned(16))) v4f sx[kHeadGroups][kQuarters][kQuarters - 1][kWave];
   // probabilities (fp16) of a tile: [head group][head][token], rows padded to 80 bytes
   __shared__ __attribute__((aligned(16))) uint8_t ps[kHeadGroups * 32 * kPsRow];
-  // FP8: pool rows of the split's selected entries in order (-1: no visible token), padded with
-  // -1 to whole tiles (a split never spans more than k <= DSA_MAX_TOPK entries)
-  __shared__ __attribute__((aligned(16))) int32_t plist[G::kFp8 ? DSA_MAX_TOPK : 4];
+  // pool rows of the split's selected entries in order (-1: no visible token), padded with -1 to
+  // whole tiles (a split never spans more than k <= DSA_MAX_TOPK entries)
+  __shared__ __attribute__((aligned(16))) int32_t plist[DSA_MAX_TOPK];
   // per head: each quarter's largest logit and its probability sum (relative to that logit)
   __shared__ __attribute__((aligned(16))) float mqs[kHeadGroups][32][kQuarters];
   __shared__ __attribute__((aligned(16))) float lqs[kHeadGroups][32][kQuarters];
-  const Stage stages[6] = {{raw0, tsc0, valid0}, {raw1, tsc1, valid1}, {raw2, tsc2, valid2},
-                           {raw3, tsc3, valid3}, {raw4, tsc4, valid4}, {raw5, tsc5, valid5}};
+  const Stage stages[6] = {{raw0, tsc0}, {raw1, tsc1}, {raw2, tsc2},
+                           {raw3, tsc3}, {raw4, tsc4}, {raw5, tsc5}};
 
   const int row = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -405,8 +357,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
   // A row without a token gathers a spare row whose data is never used: a pool row that depends
   // on the workgroup and wave (never one row for everybody: thousands of requests to one address
-  // would queue on one memory channel); NVFP4 takes the wave's first real row of the tile instead
-  // when it has one.
+  // would queue on one memory channel).
   const int ph_spread = __builtin_amdgcn_readfirstlane(
       (int)(((int64_t)blockIdx.x * 7919 + (int64_t)blockIdx.y * 131 + wave * 17) % a.pool.tokens));
   // The pool row of the split's selected entry jj, or -1 where there is none (past the split's
@@ -431,48 +382,9 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     }
     return ph;
   };
-  // NVFP4: pool rows of this wave's gathers for tiles [tb, tb + kBatchTiles) of the split (lane
-  // 3T + r: tile tb + T, row wave + 12r), or -1 where there is no visible selected token.
-  auto load_batch = [&](int tb) {
-    const int T = lane / kRowsPerWave, r = lane % kRowsPerWave;
-    const int t = wave + kWavesM * r;
-    const int jj = j0 + kTile * (tb + T) + t;
-    const bool in = T < kBatchTiles && t < kTile && jj < j1;
-    int ph = -1;
-    if (PHYS) {
-      // unconditional (entry 0 stands in for lanes without a slot), so that the query loads
-      // behind it are in flight at the same time
-      const int jc = in ? jj : 0;
-      const int v = *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(prow) +
-                                                      (uint32_t)(4 * jc));  // scalar base
-      ph = (in && v < a.pool.tokens) ? v : -1;
-      if (in && v >= a.pool.tokens && a.status) atomicOr(a.status, DSA_DEVERR_POOL_ROW);
-    } else if (in) {
-      const int s = idx[jj];
-      if (s >= 0 && s < nvis) {
-        const int b = bt[s / kBlock];
-        const bool ok = b >= 0 && (int64_t)b * kBlock < a.pool.tokens;
-        ph = ok ? b * kBlock + (s % kBlock) : -1;
-        if (!ok && a.status) atomicOr(a.status, DSA_DEVERR_BLOCK_ID);
-      }
-    }
-    const int first = __shfl(ph, kRowsPerWave * T);  // row 0 of this wave in the same tile
-    const int src = ph >= 0 ? ph : (first >= 0 ? first : ph_spread);
-    const int slot = src & (kBlock - 1);
-    constexpr int kLat = G::kFp8 ? DSA_MLA_DQK : DSA_MLA_DQK / 2;  // latent bytes per token
-    constexpr int kScl = G::kFp8 ? 4 : DSA_MLA_DQK / 16;            // scale bytes per token
-    const uint64_t off = (uint64_t)(src >> 6) * (uint64_t)a.pool.row_bytes +
-                         (uint64_t)a.pool.lat_off + (uint64_t)(slot * kLat);
-    GatherSrc g;
-    g.lo = (uint32_t)off;
-    g.hi = (uint32_t)(off >> 32) | (ph >= 0 ? 0x80000000u : 0u);
-    g.scl = (uint32_t)(a.pool.lat_scale_off - a.pool.lat_off) + (uint32_t)slot * kScl -
-            (uint32_t)slot * kLat;
-    return g;
-  };
 
-  // Prologue: the query loads go first (unconditional), the pool rows (FP8: the split's whole
-  // list; NVFP4: the first batches) right behind them, so both round trips overlap.
+  // Prologue: the query loads go first (unconditional), the split's pool rows right behind them,
+  // so both round trips overlap.
   // Q^T fragments (B operand) of this wave's quarter of the contraction
   const int kd = kQuarterDims * qt;  // first dim of the quarter (wave-uniform)
   v8bf qf[kQkSteps];
@@ -483,9 +395,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       qf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qr + 16 * i));
   }
   asm volatile("" ::: "memory");  // keep the query loads ahead of the pool-row loads
-  int tb = 0;
-  GatherSrc pv = {0u, 0u, 0u}, pv_next = {0u, 0u, 0u};
-  if constexpr (G::kFp8) {
+  {
     // the split's pool rows, resolved once: every load in flight at once, then one LDS barrier
     constexpr int kIters = (DSA_MAX_TOPK + kThreadsM - 1) / kThreadsM;
     int ph[kIters];
@@ -504,20 +414,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
     for (int i = 0; i < kQkSteps; ++i) asm volatile("" ::"v"(qf[i]));
 #pragma unroll
     for (int T = 0; T < kAhead; ++T)
-      if (T < ntiles) issue_tile_fp8(stages[T], plist + kTile * T, a, wave, lane, ph_spread);
-  } else {
-    pv = load_batch(0);
-    pv_next = ntiles > kBatchTiles ? load_batch(kBatchTiles) : pv;
-    // The pool rows and the query arrive together (one wait, before the first gather is issued:
-    // the gathers are invisible to the compiler, and a wait of its own behind them would be a
-    // full drain of the pipeline).
-#pragma unroll
-    for (int i = 0; i < kQkSteps; ++i)
-      asm volatile("" ::"v"(qf[i]), "v"(pv.lo), "v"(pv.hi), "v"(pv.scl), "v"(pv_next.lo),
-                   "v"(pv_next.hi), "v"(pv_next.scl));
-#pragma unroll
-    for (int T = 0; T < kAhead; ++T)
-      if (T < ntiles) issue_tile<LFMT>(stages[T], pv, T, a, lane);
+      if (T < ntiles) issue_tile<LFMT>(stages[T], plist + kTile * T, a, wave, lane, ph_spread);
   }
 
   // O^T (dims x heads) of this wave: dims [128 qt + 32 dt, +32) x the group's 32 heads
@@ -540,7 +437,7 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       {
         const int newer = min(kAhead - 1, ntiles - 1 - (j - j0) / kTile);
         static_assert(kAhead - 1 <= 4, "wait counts below");
-        constexpr int kG = kGathersPerWave<LFMT>;
+        constexpr int kG = G::kGathers;
         if (newer >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kG) : "memory");
         else if (newer == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kG) : "memory");
         else if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kG) : "memory");
@@ -550,11 +447,11 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       lds_barrier();  // everyone's part landed; the previous tile's readers are done
       const int tl = opaque((int)threadIdx.x);
       const int ln = tl & 63, nl = ln & 31, hl = ln >> 5;
-      const int32_t* rows = G::kFp8 ? plist + (j - j0) : cur.valid;  // >= 0: a token
+      const int32_t* rows = plist + (j - j0);  // >= 0: a token
       if constexpr (G::kFp8)
         prep_fp8(cur, rows, __ballot(rows[nl] < 0), tl);
       else
-        build_nvfp4(cur, ct, ht, tl);
+        build_nvfp4(cur, rows, ct, ht, tl);
       if constexpr (!G::kFp8) lds_barrier();  // the QK operands come from the decoded tile
 
       // this wave's quarter of S^T (32 tokens x the group's 32 heads)
@@ -689,22 +586,13 @@ __global__ __launch_bounds__(kThreadsM) void sparse_mla_kernel(MlaArgs a) {
       // queue full stalls here, where it would otherwise wait at the next barrier.
       {
         const int T = (j - j0) / kTile + kAhead;
-        if constexpr (G::kFp8) {
-          if (T < ntiles)
-            issue_tile_fp8(stages[(s + kAhead) % kStages], plist + kTile * T, a, wave, ln, ph_spread);
-        } else {
-          if (T - tb == kBatchTiles) {  // next batch of pool rows (loaded one batch ahead)
-            tb += kBatchTiles;
-            pv = pv_next;
-            if (tb + kBatchTiles < ntiles) pv_next = load_batch(tb + kBatchTiles);
-          }
-          if (T < ntiles) issue_tile<LFMT>(stages[(s + kAhead) % kStages], pv, T - tb, a, ln);
-        }
+        if (T < ntiles)
+          issue_tile<LFMT>(stages[(s + kAhead) % kStages], plist + kTile * T, a, wave, ln, ph_spread);
       }
     }
   }
 
-  // the gathers issued ahead of the last tiles (dummies) land before the workgroup ends
+  // the gathers issued ahead of the last tiles land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // lane holds O^T[128 qt + 32 dt + 8 b + 4 hi + i][head] in o[dt][4 b + i]
