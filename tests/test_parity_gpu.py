@@ -73,6 +73,18 @@ def test_short_rows_all_scores_tied():
     assert np.array_equal(idx[0], np.arange(2048)) and np.array_equal(idx[1], np.arange(2048))
 
 
+@pytest.mark.parametrize("rows", [3, 4, 31, 32])
+def test_split_combine_at_its_workgroup_size_boundaries(rows):
+    # the split combine runs one-wave workgroups below 4 rows, two-wave ones below 32 and
+    # eight-wave ones from 32 on: batches on each side of both boundaries, against the oracle
+    print(f"\n[case] combine boundary rows={rows}", flush=True)
+    rng = np.random.default_rng(700 + rows)
+    lens = [int(x) for x in rng.integers(2100, 12000, rows)]
+    wl = _one_row_per_seq(f"cmb{rows}", 700 + rows, lens)
+    layer, _, _ = run_gpu(wl)
+    check_workload(wl, layer)
+
+
 def test_decode_without_scorer_histogram():
     wl = _one_row_per_seq("nohist", 42, [3000, 70000, 129])
     layer, _, _ = run_gpu(wl, use_hist=False)
